@@ -1,0 +1,43 @@
+"""Constants of the attention contract the oracle checks against.
+
+P modes (where the softmax weights are rounded before they multiply V):
+  P_FP32    no rounding (decode: "fp32 accumulate", partials per 256-key chunk)
+  P_BF16    P = bf16(p)                      (sliding-layer prompt tiles)
+  P_BF16X2  P = bf16(p) + bf16(p - bf16(p))  ("P to 2^-16 as two bf16 halves",
+            TensorFold PR #1183, squashed commit bodies, the window_rows note;
+            read as 16 significant bits kept in two bf16 halves)
+
+Key block KB: in prompt tiles the softmax keeps a running row maximum that is
+updated once per block of KB keys, blocks aligned to absolute key positions
+(key j is in block j // KB), and P is rounded against the running maximum of
+its own block.  Which maximum P is rounded against changes the rounded value,
+so KB is part of the contract: the pages fix the online softmax per block
+(PR #975, "maxes and probabilities cross once a block") but not its size.
+This library's kernels use the sizes below; its C-ABI reports them through
+attn_prefill_key_block(), and the tests check that both agree.
+
+Error radius (the range fp32 allows, after PR #1183's attention_range note):
+  the kernel's fp32 probabilities p carry a relative error up to EPS_P (score
+  rounding in the fp32 dot product, the scale product, exp2); the weighted sum
+  of V and the row sum carry EPS_ACC relative to the sum of absolute terms.
+"""
+
+P_FP32, P_BF16, P_BF16X2 = 0, 1, 2
+
+DECODE_CHUNK = 256                 # slots per decode partial (window_rows note)
+
+PREFILL_KEY_BLOCK = {              # (head_dim, p_mode) -> KB
+    (256, P_BF16): 64,
+    (256, P_BF16X2): 64,
+    (512, P_BF16): 32,
+    (512, P_BF16X2): 32,
+}
+
+EPS_P = 2.0 ** -20
+EPS_ACC = 2.0 ** -21
+ULP_SLACK = 1                      # ordered-bits steps allowed past the range
+MEAN_REL_ERR_MAX = 1e-3
+
+
+def key_block(head_dim: int, p_mode: int) -> int:
+    return PREFILL_KEY_BLOCK[(head_dim, p_mode)]
