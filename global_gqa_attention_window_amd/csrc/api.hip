@@ -1,0 +1,165 @@
+// C ABI of the attention library: argument checks, then launches on the
+// caller's stream.  Declarations and the meaning of every argument are in
+// include/gqa_attn.h.  Every check runs before any HIP call, so a refused call
+// touches neither the device nor the stream (the pages' practice of refusing
+// unsupported geometries by name, and of validating sizes before any cast:
+// TensorFold PR #975, owner review).
+#include "../../include/gqa_attn.h"
+
+#include <math.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr long long kMaxBytes = 1LL << 46;   // 64 TiB: far past any device
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_heads(int Hq, int Hkv, int D) {
+    if (D != 256 && D != 512) return ATTN_E_HEAD_DIM;
+    if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Hq / Hkv > 16) return ATTN_E_GQA;
+    return ATTN_OK;
+}
+
+// bytes of one [n][h][len][D] bf16 tensor, or -1 past kMaxBytes
+long long tensor_bytes(long long n, long long h, long long len, long long D) {
+    if (n < 0 || h < 0 || len < 0) return -1;
+    long long b = 2 * D;
+    for (long long f : {n, h, len}) {
+        if (f != 0 && b > kMaxBytes / f) return -1;
+        b *= f;
+    }
+    return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_E_NULL: return "ATTN_E_NULL";
+        case ATTN_E_HEAD_DIM: return "ATTN_E_HEAD_DIM";
+        case ATTN_E_GQA: return "ATTN_E_GQA";
+        case ATTN_E_WINDOW: return "ATTN_E_WINDOW";
+        case ATTN_E_CACHE: return "ATTN_E_CACHE";
+        case ATTN_E_ALIGN: return "ATTN_E_ALIGN";
+        case ATTN_E_WORKSPACE: return "ATTN_E_WORKSPACE";
+        case ATTN_E_P_MODE: return "ATTN_E_P_MODE";
+        case ATTN_E_RANGE: return "ATTN_E_RANGE";
+        case ATTN_E_LAUNCH: return "ATTN_E_LAUNCH";
+        case ATTN_E_UNSUPPORTED: return "ATTN_E_UNSUPPORTED";
+        default: return "ATTN_E_UNKNOWN";
+    }
+}
+
+size_t attn_decode_workspace_bytes(int n_seq, int n_q_heads, int head_dim,
+                                   int cache_cap) {
+    if (n_seq < 0 || cache_cap < 1 || n_q_heads < 1 || (head_dim != 256 && head_dim != 512))
+        return 0;
+    const long long nch = ((long long)cache_cap + ATTN_DECODE_CHUNK - 1) / ATTN_DECODE_CHUNK;
+    const long long units = (long long)n_seq * n_q_heads * nch;
+    if (units > kMaxBytes / (4 * (head_dim + 2))) return 0;
+    return decode_workspace_bytes(n_seq, n_q_heads, head_dim, cache_cap);
+}
+
+int attn_decode(void* out, const void* q, const void* k_cache,
+                const void* v_cache, const int32_t* pos, int n_seq,
+                int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
+                int ring, int window, float scale, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+    if (st != ATTN_OK) return st;
+    if (n_seq < 0 || (ring != 0 && ring != 1) || !isfinite(scale)) return ATTN_E_RANGE;
+    if (cache_cap < 1) return ATTN_E_CACHE;
+    if (window < 0 || (ring && window > cache_cap)) return ATTN_E_WINDOW;
+    if (tensor_bytes(n_seq, n_kv_heads, cache_cap, head_dim) < 0 ||
+        tensor_bytes(n_seq, n_q_heads, 1, head_dim) < 0)
+        return ATTN_E_RANGE;
+    if (n_seq == 0) return ATTN_OK;
+    if (!out || !q || !k_cache || !v_cache || !pos) return ATTN_E_NULL;
+    if (!workspace) return ATTN_E_WORKSPACE;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(pos) & 3u) != 0)
+        return ATTN_E_ALIGN;
+    const size_t need = attn_decode_workspace_bytes(n_seq, n_q_heads, head_dim, cache_cap);
+    if (need == 0) return ATTN_E_RANGE;
+    if (workspace_bytes < need) return ATTN_E_WORKSPACE;
+    if (n_seq > 65535 || n_kv_heads > 65535 ||
+        (cache_cap + ATTN_DECODE_CHUNK - 1) / ATTN_DECODE_CHUNK > 0x7FFFFFFF / 2)
+        return ATTN_E_RANGE;
+    hipError_t e = launch_decode(
+        static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+        static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+        pos, n_seq, n_q_heads, n_kv_heads, head_dim, cache_cap, ring, window,
+        scale, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+int attn_prefill_key_block(int head_dim, int p_mode) {
+    if (head_dim != 256 && head_dim != 512) return ATTN_E_HEAD_DIM;
+    if (p_mode != ATTN_P_BF16 && p_mode != ATTN_P_BF16X2) return ATTN_E_P_MODE;
+    return prefill_key_block(head_dim, p_mode);
+}
+
+int attn_prefill(void* out, const void* q, const void* k_cache,
+                 const void* v_cache, int pos0, int n_rows, int n_q_heads,
+                 int n_kv_heads, int head_dim, int cache_cap, int ring,
+                 int window, float scale, int p_mode,
+                 const int32_t* last_key, void* stream) {
+    int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+    if (st != ATTN_OK) return st;
+    if (p_mode != ATTN_P_BF16 && p_mode != ATTN_P_BF16X2) return ATTN_E_P_MODE;
+    if (last_key) return ATTN_E_UNSUPPORTED;
+    if (n_rows < 0 || pos0 < 0 || (ring != 0 && ring != 1) || !isfinite(scale))
+        return ATTN_E_RANGE;
+    if (cache_cap < 1) return ATTN_E_CACHE;
+    if (window < 0) return ATTN_E_WINDOW;
+    if (ring) {
+        if (window == 0 || window > cache_cap) return ATTN_E_WINDOW;
+        if ((long long)cache_cap < (long long)window + n_rows - 1) return ATTN_E_CACHE;
+    } else if ((long long)pos0 + n_rows > cache_cap) {
+        return ATTN_E_CACHE;
+    }
+    if (tensor_bytes(1, n_kv_heads, cache_cap, head_dim) < 0 ||
+        tensor_bytes(n_rows, n_q_heads, 1, head_dim) < 0)
+        return ATTN_E_RANGE;
+    if (n_rows == 0) return ATTN_OK;
+    if (!out || !q || !k_cache || !v_cache) return ATTN_E_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return ATTN_E_ALIGN;
+    hipError_t e = launch_prefill(
+        static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+        static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+        pos0, n_rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring, window,
+        scale, p_mode, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+int attn_cache_write(void* k_cache, void* v_cache, const void* k,
+                     const void* v, int pos0, int n_rows, int n_kv_heads,
+                     int head_dim, int cache_cap, int ring, void* stream) {
+    if (head_dim != 256 && head_dim != 512) return ATTN_E_HEAD_DIM;
+    if (n_kv_heads < 1) return ATTN_E_GQA;
+    if (n_rows < 0 || pos0 < 0 || (ring != 0 && ring != 1)) return ATTN_E_RANGE;
+    if (cache_cap < 1) return ATTN_E_CACHE;
+    if (ring ? n_rows > cache_cap : (long long)pos0 + n_rows > cache_cap)
+        return ATTN_E_CACHE;
+    if (tensor_bytes(1, n_kv_heads, cache_cap, head_dim) < 0 ||
+        tensor_bytes(n_rows, n_kv_heads, 1, head_dim) < 0)
+        return ATTN_E_RANGE;
+    if (n_rows == 0) return ATTN_OK;
+    if (!k_cache || !v_cache || !k || !v) return ATTN_E_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k) || !aligned16(v))
+        return ATTN_E_ALIGN;
+    hipError_t e = launch_cache_write(
+        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache),
+        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), pos0,
+        n_rows, n_kv_heads, head_dim, cache_cap, ring, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Device helpers shared by the gfx950 attention kernels.
+//
+// Matrix-core conventions (CDNA3/CDNA4 16x16 MFMA, wave64):
+//   v_mfma_f32_16x16x32_bf16  A 16x32, B 32x16: lane l supplies row/column
+//       l % 16 and eight reduction indices picked by l / 16; the reduction
+//       index a lane supplies is the same slot for A and B, so any one-to-one
+//       assignment of reduction indices to (l / 16, element) is a valid dot
+//       product.  C 16x16: lane l holds rows 4 * (l / 16) + i, column l % 16.
+//   v_mfma_f32_16x16x4_f32    A 16x4: lane l holds A[l % 16][l / 16];
+//       B 4x16: B[l / 16][l % 16]; C as above.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define ATTN_DEV __device__ __forceinline__
+
+ATTN_DEV float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+ATTN_DEV float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+ATTN_DEV uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+ATTN_DEV float bf16_round_f32(float f) {
+    return __uint_as_float(f32_to_bf16_bits(f) << 16);
+}
+
+ATTN_DEV uint32_t pack_bf16x2(uint32_t lo_bits, uint32_t hi_bits) {
+    return (lo_bits & 0xFFFFu) | (hi_bits << 16);
+}
+
+ATTN_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+ATTN_DEV f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+ATTN_DEV f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+ATTN_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// butterfly over the four lanes l, l^16, l^32, l^48 (same l % 16)
+ATTN_DEV float xmax4(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+ATTN_DEV float xsum4(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+ATTN_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+ATTN_DEV void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// log2(e) as float: scores are scaled by scale * log2(e) and exponentiated
+// with exp2, so exp(scale * s - m) = exp2(scale * log2e * s - m').
+#define ATTN_LOG2E 1.4426950408889634f

@@ -1,0 +1,25 @@
+// Launchers of the gfx950 kernels, called by the C ABI (api.hip) after it has
+// checked every argument.  Shapes reaching these functions are valid.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+size_t decode_workspace_bytes(int S, int Hq, int D, int cap);
+
+hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* kc,
+                         const uint16_t* vc, const int32_t* pos, int S, int Hq,
+                         int Hkv, int D, int cap, int ring, int window,
+                         float scale, void* ws, hipStream_t stream);
+
+int prefill_key_block(int D, int p_mode);
+
+hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
+                          const uint16_t* vc, int pos0, int n_rows, int Hq,
+                          int Hkv, int D, int cap, int ring, int window,
+                          float scale, int p_mode, hipStream_t stream);
+
+hipError_t launch_cache_write(uint16_t* kc, uint16_t* vc, const uint16_t* k,
+                              const uint16_t* v, int pos0, int n_rows, int Hkv,
+                              int D, int cap, int ring, hipStream_t stream);

@@ -1,0 +1,181 @@
+/*
+ * gqa_attn.h -- C ABI of an MI355X (gfx950) library for Gemma-4-style
+ * grouped-query attention over a KV cache.
+ *
+ * The method (TensorFold pull-request pages):
+ *   - PR #1183 "cuda gemma4: images on the 12B, and LayerNorm rows to 8192
+ *     wide", squashed commit bodies, the window_rows notes: decode splits a
+ *     head's keys into 256-key chunks, each leaving a partial (max, sum,
+ *     accumulator), merged in chunk order; prompt tiles score over 128-dim
+ *     slices; P may be kept to 16 bits as two bf16 halves; at head dim 512 no
+ *     window applies, over a linear cache of up to 262144 keys, GQA 8 and 16.
+ *   - PR #1183, same commit bodies, the Gemma 4 CUDA engine note: a sliding
+ *     ring per sliding layer (window plus a chunk), a linear cache per global
+ *     layer, prompt chunks of up to 512 rows; positions and slots of a decode
+ *     forward are read on the device.
+ *   - PR #975 "Gemma 4 12B on the native Metal engine", commit bodies: the
+ *     cache is written before prompt attention, which takes its first new
+ *     key from the metadata; 16-row query tiles under causal and sliding-
+ *     window masks with an online softmax whose maxima and probabilities
+ *     cross once a key block; value reads stop at the last written key.
+ *   - PR #1184 "z-lab's DFlash drafter on the 31B", gotchas: the cache keeps
+ *     a context's heads one capacity apart.
+ *
+ * Conventions for every call:
+ *   - bf16 tensors are raw 16-bit patterns (uint16 storage), row-major.
+ *   - Pointers marked "device" are device memory of the current HIP device;
+ *     the library allocates nothing, keeps no state and is thread-safe.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the null stream.
+ *     Every compute call only enqueues work on `stream` and returns.
+ *   - Arguments are checked before anything is launched; a refusal returns
+ *     a negative ATTN_E_* status and launches nothing.  A launch failure
+ *     returns ATTN_E_LAUNCH.  No C++ exception crosses this interface.
+ *   - Device-side values (decode positions) are trusted: they select which
+ *     slots count, but every slot read lies inside [0, cache_cap) whatever
+ *     they hold.
+ *
+ * Notation: S streams, Hq query heads, Hkv KV heads, G = Hq / Hkv query heads
+ * per KV head (query head h uses KV head h / G), D head dim, cap cache slots.
+ * Cache layout: [S][Hkv][cap][D] (decode) or [Hkv][cap][D] (one prompt
+ * stream): heads cap apart.  Linear cache: slot j holds position j.  Ring of
+ * cap slots: position p lives in slot p mod cap.
+ * A row at position t attends key positions p with p <= t and, when the
+ * window W > 0, t - p < W (the row itself and the W-1 before it).
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+enum {
+    ATTN_OK = 0,
+    ATTN_E_NULL = -1,        /* a required pointer is NULL                  */
+    ATTN_E_HEAD_DIM = -2,    /* head_dim not 256 or 512                     */
+    ATTN_E_GQA = -3,         /* Hq, Hkv < 1, Hq % Hkv != 0 or G > 16        */
+    ATTN_E_WINDOW = -4,      /* window < 0, ring window > cap, or a prompt
+                                ring with no window                         */
+    ATTN_E_CACHE = -5,       /* cap < 1, or a prompt chunk that does not fit
+                                (linear: pos0 + n_rows > cap; ring:
+                                cap < window + n_rows - 1)                  */
+    ATTN_E_ALIGN = -6,       /* a pointer not 16-byte aligned               */
+    ATTN_E_WORKSPACE = -7,   /* decode workspace NULL or too small          */
+    ATTN_E_P_MODE = -8,      /* unknown P mode, or one the call cannot take */
+    ATTN_E_RANGE = -9,       /* a count < 0, pos0 < 0, non-finite scale, or
+                                sizes whose byte offsets overflow 64 bits   */
+    ATTN_E_LAUNCH = -10,     /* the HIP runtime refused a launch            */
+    ATTN_E_UNSUPPORTED = -11 /* an argument reserved for a later extension  */
+};
+
+/* where softmax probabilities are rounded before they multiply V */
+enum {
+    ATTN_P_FP32 = 0,   /* not rounded (decode)                               */
+    ATTN_P_BF16 = 1,   /* P = bf16(p)                                        */
+    ATTN_P_BF16X2 = 2  /* P = bf16(p) + bf16(p - bf16(p)): two bf16 halves    */
+};
+
+/* slots per decode partial: the 256-key chunks of the window_rows note */
+#define ATTN_DECODE_CHUNK 256
+
+/*
+ * Bytes of device workspace attn_decode needs: one fp32 partial
+ * (max, sum, accumulator[D]) per (stream, query head, 256-slot chunk), the
+ * scratch PR #975's decode notes size by the number of chunks.
+ * Returns 0 for arguments attn_decode would refuse.
+ */
+size_t attn_decode_workspace_bytes(int n_seq, int n_q_heads, int head_dim,
+                                   int cache_cap);
+
+/*
+ * One decode row per stream (PR #1183 window_rows notes; PR #975 decode
+ * attention commits).  For stream s and query head h, with t = pos[s]:
+ * keys are the cache slots whose position is attended by a row at t; each
+ * 256-slot chunk c yields m_c = max score, l_c = sum exp(s - m_c) and
+ * acc_c = sum exp(s - m_c) v; chunks merge in ascending order over the
+ * largest m_c; out = bf16(sum e^(m_c - M) acc_c / sum e^(m_c - M) l_c).
+ * Scores are scale * q.k with fp32 accumulation; probabilities are not
+ * rounded to bf16 (carried to 16 significant bits for the matrix cores).
+ * A row with no attended key (t < 0) gives +0.
+ *
+ *   out        device bf16 [S][Hq][D], written
+ *   q          device bf16 [S][Hq][D]
+ *   k_cache    device bf16 [S][Hkv][cap][D]
+ *   v_cache    device bf16 [S][Hkv][cap][D]
+ *   pos        device int32 [S]: each stream's row position t
+ *   n_seq      S >= 0 (0 launches nothing)
+ *   ring       0 linear cache, 1 ring of cap slots
+ *   window     W >= 0, 0 = none; a ring needs W <= cap
+ *   scale      finite fp32 score scale
+ *   workspace  device, >= attn_decode_workspace_bytes(S, Hq, D, cap) bytes,
+ *              16-byte aligned; contents on entry are ignored
+ */
+int attn_decode(void* out, const void* q, const void* k_cache,
+                const void* v_cache, const int32_t* pos, int n_seq,
+                int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
+                int ring, int window, float scale, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
+ * Prompt attention for one stream's chunk of n_rows rows at positions
+ * pos0 .. pos0 + n_rows - 1 (PR #975 prompt attention commits; PR #1183
+ * window_rows notes).  The chunk's own keys and values must already be in
+ * the cache (attn_cache_write).  Each row attends its positions (causal,
+ * sliding window W when W > 0) in blocks of KB = attn_prefill_key_block()
+ * keys aligned to absolute positions, in ascending order: the running
+ * maximum m moves once a block, p = exp(s - m), P = round(p) per p_mode is
+ * what multiplies V, the row sum takes unrounded p, and
+ * out = bf16(acc / sum).  Keys outside a tile's attended span are never
+ * read into the products (a never-written V row cannot turn into NaN).
+ *
+ *   out       device bf16 [n_rows][Hq][D], written
+ *   q         device bf16 [n_rows][Hq][D]
+ *   k_cache   device bf16 [Hkv][cap][D]
+ *   v_cache   device bf16 [Hkv][cap][D]
+ *   pos0      position of the first row, >= 0
+ *   n_rows    >= 0 (0 launches nothing)
+ *   ring      0 linear (pos0 + n_rows <= cap), 1 ring (0 < W <= cap and
+ *             cap >= W + n_rows - 1, so no row's keys are overwritten)
+ *   p_mode    ATTN_P_BF16 or ATTN_P_BF16X2
+ *   last_key  must be NULL (per-row key bounds are not implemented yet:
+ *             non-NULL returns ATTN_E_UNSUPPORTED)
+ */
+int attn_prefill(void* out, const void* q, const void* k_cache,
+                 const void* v_cache, int pos0, int n_rows, int n_q_heads,
+                 int n_kv_heads, int head_dim, int cache_cap, int ring,
+                 int window, float scale, int p_mode,
+                 const int32_t* last_key, void* stream);
+
+/*
+ * Write a chunk's new keys and values into the cache before attention
+ * (PR #975, the cache-before-attention commit): row r goes to the slot of
+ * position pos0 + r (linear: pos0 + r < cap required; ring: (pos0 + r) mod
+ * cap, and n_rows <= cap).  Bit copies, no rounding.
+ *
+ *   k_cache, v_cache  device bf16 [Hkv][cap][D], updated
+ *   k, v              device bf16 [n_rows][Hkv][D]
+ */
+int attn_cache_write(void* k_cache, void* v_cache, const void* k,
+                     const void* v, int pos0, int n_rows, int n_kv_heads,
+                     int head_dim, int cache_cap, int ring, void* stream);
+
+/*
+ * The key block KB attn_prefill uses for (head_dim, p_mode): the block at
+ * which the running maximum moves and P is rounded, which decides P's
+ * rounded values.  64 at head dim 256, 32 at head dim 512.  Returns a
+ * negative status for a head dim or P mode attn_prefill refuses.
+ */
+int attn_prefill_key_block(int head_dim, int p_mode);
+
+/* Static, NUL-terminated name of a status code ("ATTN_OK", ...). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

@@ -7,8 +7,9 @@ path (``global_gqa_attention_window_amd``) and never reads that path's outputs.
 
 Everything is float64 NumPy, rounded to bf16 only at the points the method
 names (TensorFold PR #1183 "cuda gemma4: images on the 12B ...", squashed
-commit bodies, the window_rows and attention_range notes: "float64 at the
-rounding points and the range fp32 allows").
+commit bodies, the window_rows and attention_range notes: the checker holds
+float64 values at the rounding points, with the spread fp32 arithmetic can
+reach around them).
 
 Modules
   bf16      float64 -> bf16 round-to-nearest-even, ordered bit keys

@@ -7,8 +7,8 @@ Sources (TensorFold pull-request pages):
   * PR #1183 "cuda gemma4: images on the 12B ...", squashed commit bodies,
     window_rows notes: decode splits a head's keys into 256-key chunks with a
     partial (max, sum, accumulator) each, merged in chunk order; prompt tiles
-    over 128-dim slices; P kept to 2^-16 as two bf16 halves; the checker is
-    "float64 at the rounding points and the range fp32 allows".  At head dim
+    over 128-dim slices; P kept to 16 bits as two bf16 halves; the checker
+    holds float64 at the rounding points plus the spread fp32 allows.  At head dim
     512: no window over a linear cache to 262144 keys, GQA 8 and 16.
   * PR #1183, same commit bodies, the Gemma 4 CUDA engine note: sliding
     layers use a ring (window plus a chunk) and keep each sliding layer's last

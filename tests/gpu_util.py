@@ -1,0 +1,58 @@
+"""Helpers for the GPU tests: move bf16 bit arrays to and from the device and
+call the library through its Python binding (which calls the C ABI)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def up(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def down(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy().view(np.uint16)
+
+
+def run_decode(ga, q, k, v, pos, Hkv, ring, window, scale, ws_pad=0):
+    S, Hq, D = q.shape
+    cap = k.shape[2]
+    out = torch.empty((S, Hq, D), dtype=torch.int16, device=DEV)
+    nbytes = ga.attn_decode_workspace_bytes(S, Hq, D, cap)
+    ws = torch.empty(nbytes + ws_pad, dtype=torch.uint8, device=DEV)
+    ga.attn_decode(out, up(q), up(k), up(v), up(np.asarray(pos, np.int32)), S, Hq, Hkv,
+                   D, cap, ring, window, scale, ws)
+    return down(out)
+
+
+def run_prefill(ga, q, k, v, Hkv, cap, ring, window, scale, p_mode, chunk,
+                pos0=0, caches=None):
+    """Prompt rows pos0.. in chunks: cache write, then attention, per chunk."""
+    n, Hq, D = q.shape
+    if caches is None:
+        kc = torch.zeros((Hkv, cap, D), dtype=torch.int16, device=DEV)
+        vc = torch.zeros_like(kc)
+    else:
+        kc, vc = caches
+    qd, kd, vd = up(q), up(k[pos0:pos0 + n]), up(v[pos0:pos0 + n])
+    out = torch.empty((n, Hq, D), dtype=torch.int16, device=DEV)
+    for r0 in range(0, n, chunk):
+        m = min(chunk, n - r0)
+        ga.attn_cache_write(kc, vc, kd[r0:r0 + m], vd[r0:r0 + m], pos0 + r0, m, Hkv, D,
+                            cap, ring)
+        ga.attn_prefill(out[r0:r0 + m], qd[r0:r0 + m], kc, vc, pos0 + r0, m, Hq, Hkv, D,
+                        cap, ring, window, scale, p_mode)
+    return down(out), (kc, vc)

@@ -1,0 +1,164 @@
+"""Host-side checks of the C ABI (no GPU, no compute calls).
+
+The library must load, export every function include/gqa_attn.h declares,
+refuse bad arguments with the named status before touching the device, and
+report the key block the oracle's contract names.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle.contract import DECODE_CHUNK, P_BF16, P_BF16X2, P_FP32, key_block
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+LIB = os.path.join(ROOT, "global_gqa_attention_window_amd", "libgqa_attn.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", src)))
+
+
+def _status(name):
+    src = open(HEADER).read()
+    return int(re.search(rf"\b{name}\s*=\s*(-?\d+)", src).group(1))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ctypes.CDLL(LIB)
+
+
+@pytest.fixture(scope="module")
+def ga():
+    import global_gqa_attention_window_amd as ga
+    return ga
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared()
+    assert set(names) >= {"attn_decode", "attn_prefill", "attn_cache_write",
+                          "attn_decode_workspace_bytes", "attn_prefill_key_block",
+                          "attn_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(ga):
+    for name in ["ATTN_OK", "ATTN_E_NULL", "ATTN_E_HEAD_DIM", "ATTN_E_GQA",
+                 "ATTN_E_WINDOW", "ATTN_E_CACHE", "ATTN_E_ALIGN", "ATTN_E_WORKSPACE",
+                 "ATTN_E_P_MODE", "ATTN_E_RANGE", "ATTN_E_LAUNCH", "ATTN_E_UNSUPPORTED"]:
+        assert ga.attn_status_string(_status(name)) == name
+    assert ga.attn_status_string(12345) == "ATTN_E_UNKNOWN"
+
+
+def test_key_block_matches_contract(ga):
+    for D in (256, 512):
+        for pm in (P_BF16, P_BF16X2):
+            assert ga.attn_prefill_key_block(D, pm) == key_block(D, pm)
+    assert ga._lib.attn_prefill_key_block(128, P_BF16) == _status("ATTN_E_HEAD_DIM")
+    assert ga._lib.attn_prefill_key_block(256, P_FP32) == _status("ATTN_E_P_MODE")
+    assert ga.ATTN_DECODE_CHUNK == DECODE_CHUNK
+
+
+def test_workspace_bytes(ga):
+    # one fp32 (max, sum, acc[D]) per (stream, query head, 256-slot chunk)
+    assert ga.attn_decode_workspace_bytes(8, 32, 512, 32768) == 8 * 32 * 128 * 514 * 4
+    assert ga.attn_decode_workspace_bytes(1, 8, 256, 512) == 1 * 8 * 2 * 258 * 4
+    assert ga.attn_decode_workspace_bytes(1, 8, 256, 300) == 1 * 8 * 2 * 258 * 4
+    assert ga.attn_decode_workspace_bytes(1, 8, 128, 512) == 0
+    assert ga.attn_decode_workspace_bytes(1, 8, 256, 0) == 0
+    assert ga.attn_decode_workspace_bytes(-1, 8, 256, 10) == 0
+
+
+# fake device pointers: refusals happen before any use, so these are never read
+P = 1 << 20
+
+
+def _decode(ga, **kw):
+    a = dict(out=P, q=P, k=P, v=P, pos=P, S=1, Hq=8, Hkv=1, D=256, cap=512, ring=0,
+             window=0, scale=0.0625, ws=P, ws_bytes=1 << 30)
+    a.update(kw)
+    return ga._lib.attn_decode(a["out"], a["q"], a["k"], a["v"], a["pos"], a["S"], a["Hq"],
+                               a["Hkv"], a["D"], a["cap"], a["ring"], a["window"], a["scale"],
+                               a["ws"], a["ws_bytes"], None)
+
+
+def _prefill(ga, **kw):
+    a = dict(out=P, q=P, k=P, v=P, pos0=0, n=128, Hq=32, Hkv=4, D=256, cap=1152, ring=1,
+             window=1024, scale=0.0625, p_mode=P_BF16, last=None)
+    a.update(kw)
+    return ga._lib.attn_prefill(a["out"], a["q"], a["k"], a["v"], a["pos0"], a["n"], a["Hq"],
+                                a["Hkv"], a["D"], a["cap"], a["ring"], a["window"],
+                                a["scale"], a["p_mode"], a["last"], None)
+
+
+def _cw(ga, **kw):
+    a = dict(kc=P, vc=P, k=P, v=P, pos0=0, n=128, Hkv=4, D=256, cap=1152, ring=1)
+    a.update(kw)
+    return ga._lib.attn_cache_write(a["kc"], a["vc"], a["k"], a["v"], a["pos0"], a["n"],
+                                    a["Hkv"], a["D"], a["cap"], a["ring"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), "ATTN_E_NULL"), (dict(q=None), "ATTN_E_NULL"),
+    (dict(k=None), "ATTN_E_NULL"), (dict(v=None), "ATTN_E_NULL"),
+    (dict(pos=None), "ATTN_E_NULL"), (dict(ws=None), "ATTN_E_WORKSPACE"),
+    (dict(D=128), "ATTN_E_HEAD_DIM"), (dict(D=384), "ATTN_E_HEAD_DIM"),
+    (dict(Hq=12, Hkv=8), "ATTN_E_GQA"), (dict(Hq=34, Hkv=2), "ATTN_E_GQA"),
+    (dict(Hkv=0), "ATTN_E_GQA"), (dict(Hq=0), "ATTN_E_GQA"),
+    (dict(window=-1), "ATTN_E_WINDOW"), (dict(ring=1, window=513), "ATTN_E_WINDOW"),
+    (dict(cap=0), "ATTN_E_CACHE"), (dict(S=-1), "ATTN_E_RANGE"),
+    (dict(ring=2), "ATTN_E_RANGE"), (dict(scale=float("inf")), "ATTN_E_RANGE"),
+    (dict(scale=float("nan")), "ATTN_E_RANGE"),
+    (dict(out=P + 2), "ATTN_E_ALIGN"), (dict(k=P + 8), "ATTN_E_ALIGN"),
+    (dict(ws=P + 4), "ATTN_E_ALIGN"), (dict(pos=P + 2), "ATTN_E_ALIGN"),
+    (dict(ws_bytes=100), "ATTN_E_WORKSPACE"),
+    (dict(S=1 << 20, cap=1 << 30, Hkv=1 << 10, Hq=1 << 10), "ATTN_E_RANGE"),
+])
+def test_decode_refusals(ga, kw, status):
+    assert _decode(ga, **kw) == _status(status)
+
+
+def test_decode_zero_streams_is_a_no_op(ga):
+    assert _decode(ga, S=0, out=None, q=None, ws=None) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), "ATTN_E_NULL"), (dict(k=None), "ATTN_E_NULL"),
+    (dict(D=64), "ATTN_E_HEAD_DIM"), (dict(Hq=30), "ATTN_E_GQA"),
+    (dict(p_mode=P_FP32), "ATTN_E_P_MODE"), (dict(p_mode=7), "ATTN_E_P_MODE"),
+    (dict(last=P), "ATTN_E_UNSUPPORTED"),
+    (dict(ring=1, window=0), "ATTN_E_WINDOW"), (dict(window=1153), "ATTN_E_WINDOW"),
+    (dict(window=-3), "ATTN_E_WINDOW"),
+    (dict(cap=1150), "ATTN_E_CACHE"),              # ring < window + rows - 1
+    (dict(ring=0, window=0, cap=1000, pos0=900), "ATTN_E_CACHE"),
+    (dict(cap=0), "ATTN_E_CACHE"), (dict(n=-1), "ATTN_E_RANGE"),
+    (dict(pos0=-5), "ATTN_E_RANGE"), (dict(scale=float("-inf")), "ATTN_E_RANGE"),
+    (dict(q=P + 6), "ATTN_E_ALIGN"),
+])
+def test_prefill_refusals(ga, kw, status):
+    assert _prefill(ga, **kw) == _status(status)
+
+
+def test_prefill_edges_accepted_by_checks(ga):
+    # exact fits pass the checks; n = 0 returns before any launch
+    assert _prefill(ga, n=0, out=None) == 0
+    assert _prefill(ga, ring=0, window=0, cap=1000, pos0=872, n=0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kc=None), "ATTN_E_NULL"), (dict(v=None), "ATTN_E_NULL"),
+    (dict(D=100), "ATTN_E_HEAD_DIM"), (dict(Hkv=0), "ATTN_E_GQA"),
+    (dict(ring=0, cap=1000, pos0=900), "ATTN_E_CACHE"),
+    (dict(n=1153), "ATTN_E_CACHE"), (dict(pos0=-1), "ATTN_E_RANGE"),
+    (dict(k=P + 2), "ATTN_E_ALIGN"),
+])
+def test_cache_write_refusals(ga, kw, status):
+    assert _cw(ga, **kw) == _status(status)

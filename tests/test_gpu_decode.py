@@ -1,0 +1,162 @@
+"""GPU parity of attn_decode and attn_cache_write against the CPU oracle.
+
+Every output element is checked with attn_ref.check: within one ordered bf16
+step of [bf16(o - r), bf16(o + r)] and mean relative error <= 1e-3.  Masks
+and indexing are checked bit for bit with dominating keys and NaN poison.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import run_decode, say, up, down, DEV
+from oracle import attn_ref
+from synthetic.gen import WORKLOADS, decode_inputs, f32_to_bf16_bits, randn_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ga():
+    import global_gqa_attention_window_amd as ga
+    return ga
+
+
+def _check(tag, got, ref):
+    res = attn_ref.check(got, ref["o"], ref["r"])
+    say(tag, {k: res[k] for k in ("n", "fails", "max_steps_out", "mean_rel_err", "bit_equal")})
+    assert res["ok"], (tag, res)
+
+
+@pytest.mark.parametrize("name", ["decode_g8_d256_512", "decode_sliding_ring1024",
+                                  "decode_global_32k"])
+def test_decode_workloads_full(ga, name):
+    w = WORKLOADS[name]
+    say("decode workload", name)
+    q, k, v, pos = decode_inputs(w)
+    got = run_decode(ga, q, k, v, pos, w.Hkv, w.ring, w.window, w.scale)
+    ref = attn_ref.decode(q, k, v, pos, w.Hkv, w.ring, w.window, w.scale)
+    _check(name, got, ref)
+
+
+def test_decode_262144_keys(ga):
+    w = WORKLOADS["prefill_global_32k"]
+    cap, t = w.extra["decode_cap"], w.extra["decode_pos"]
+    say("decode 262144-key linear cache, S=1, 32/2 heads, D=512")
+    rng = np.random.default_rng(w.extra["decode_seed"])
+    q = randn_bf16_bits(rng, (1, w.Hq, w.D))
+    k = randn_bf16_bits(rng, (1, w.Hkv, cap, w.D))
+    v = randn_bf16_bits(rng, (1, w.Hkv, cap, w.D))
+    got = run_decode(ga, q, k, v, [t], w.Hkv, 0, 0, w.scale)
+    ref = attn_ref.decode(q, k, v, [t], w.Hkv, 0, 0, w.scale)
+    _check("decode_262144", got, ref)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,cap,ring,window,pos", [
+    (256, 32, 4, 1000, 0, 0, [999, 0, 255, 256, 257, 511, 700, 17]),    # ragged, partial chunk
+    (256, 16, 2, 1024, 1, 1024, [1023, 5000, 70000, 1024, 1025, 3, 2047, 4096]),  # wraps
+    (256, 8, 1, 1152, 1, 1024, [8191, 1151, 1152, 100]),                 # ring of W + chunk
+    (512, 32, 2, 3000, 0, 700, [2999, 699, 700, 1500, 10, 2048, 2304, 1]),  # window linear
+    (512, 16, 1, 520, 1, 333, [519, 1000, 33, 5]),
+    (256, 12, 3, 300, 0, 0, [299, 128, 0]),                              # G = 4
+    (512, 2, 2, 256, 0, 0, [255, 100]),                                  # G = 1
+])
+def test_decode_ragged_shapes(ga, D, Hq, Hkv, cap, ring, window, pos):
+    say("decode ragged", D, Hq, Hkv, cap, ring, window, pos)
+    rng = np.random.default_rng(cap + D + Hq)
+    S = len(pos)
+    q = randn_bf16_bits(rng, (S, Hq, D))
+    k = randn_bf16_bits(rng, (S, Hkv, cap, D))
+    v = randn_bf16_bits(rng, (S, Hkv, cap, D))
+    got = run_decode(ga, q, k, v, pos, Hkv, ring, window, 0.07)
+    ref = attn_ref.decode(q, k, v, pos, Hkv, ring, window, 0.07)
+    _check(f"ragged D={D} cap={cap} ring={ring} W={window}", got, ref)
+
+
+def test_decode_empty_rows_give_zero(ga):
+    say("decode empty rows")
+    rng = np.random.default_rng(5)
+    q = randn_bf16_bits(rng, (3, 8, 256))
+    k = randn_bf16_bits(rng, (3, 1, 512, 256))
+    v = randn_bf16_bits(rng, (3, 1, 512, 256))
+    got = run_decode(ga, q, k, v, [-1, -7, 3], 1, 1, 64, 0.0625)
+    assert np.all(got[:2] == 0)
+    ref = attn_ref.decode(q, k, v, [-1, -7, 3], 1, 1, 64, 0.0625)
+    _check("empty rows", got, ref)
+
+
+@pytest.mark.parametrize("ring", [0, 1])
+def test_decode_nan_in_unattended_slots(ga, ring):
+    say("decode NaN poison, ring", ring)
+    rng = np.random.default_rng(6 + ring)
+    D, cap, W = 512, 1280, 600
+    pos = [1279, 900, 3000, 650] if ring else [1279, 900, 640, 650]
+    S = len(pos)
+    q = randn_bf16_bits(rng, (S, 16, D))
+    k = randn_bf16_bits(rng, (S, 1, cap, D))
+    v = randn_bf16_bits(rng, (S, 1, cap, D))
+    for s, t in enumerate(pos):
+        sp = attn_ref.slot_positions(t, cap, ring)
+        dead = ~attn_ref.key_valid(sp, t, W)
+        k[s, 0, dead] = 0x7FC0
+        v[s, 0, dead] = 0x7FC0
+    got = run_decode(ga, q, k, v, pos, 1, ring, W, 0.05)
+    assert not np.any(((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0))
+    ref = attn_ref.decode(q, k, v, pos, 1, ring, W, 0.05)
+    _check("nan poison", got, ref)
+
+
+@pytest.mark.parametrize("ring,t", [(0, 2999), (1, 5000), (1, 1100)])
+def test_decode_dominating_key_edges(ga, ring, t):
+    """k = 8 q at one slot: its V must come out bit for bit when attended."""
+    say("decode dominating key", ring, t)
+    rng = np.random.default_rng(8)
+    D, cap, W = 256, 1024 if ring else 3000, 777
+    slot = (lambda p: p % cap) if ring else (lambda p: p)
+    for where, inside in [(t - W + 1, True), (t - W, False), (t, True)]:
+        q = randn_bf16_bits(rng, (1, 8, D))
+        q[0, 1:] = q[0, 0]
+        k = f32_to_bf16_bits((rng.standard_normal((1, 1, cap, D)) * 0.02).astype(np.float32))
+        v = randn_bf16_bits(rng, (1, 1, cap, D))
+        qf = (q[0, 0].astype(np.uint32) << 16).view(np.float32)
+        k[0, 0, slot(where)] = f32_to_bf16_bits(8 * qf)
+        got = run_decode(ga, q, k, v, [t], 1, ring, W, 1.0)
+        ref = attn_ref.decode(q, k, v, [t], 1, ring, W, 1.0)
+        hit = np.all(got[0] == v[0, 0, slot(where)][None, :])
+        assert hit == inside, (where, inside)
+        _check(f"dominating {where}", got, ref)
+
+
+def test_decode_deterministic_and_batch_independent(ga):
+    say("decode determinism")
+    w = WORKLOADS["decode_sliding_ring1024"]
+    q, k, v, pos = decode_inputs(w)
+    a = run_decode(ga, q, k, v, pos, w.Hkv, w.ring, w.window, w.scale)
+    b = run_decode(ga, q, k, v, pos, w.Hkv, w.ring, w.window, w.scale)
+    assert np.array_equal(a, b)
+    # stream 3 alone gives the same bits as inside the batch of 8
+    c = run_decode(ga, q[3:4], k[3:4], v[3:4], pos[3:4], w.Hkv, w.ring, w.window, w.scale)
+    assert np.array_equal(a[3:4], c)
+
+
+@pytest.mark.parametrize("ring,cap,pos0,n", [(0, 4096, 1000, 512), (1, 1152, 8000, 128),
+                                             (1, 1536, 1000, 512), (0, 64, 0, 64)])
+def test_cache_write_slots_bit_exact(ga, ring, cap, pos0, n):
+    import torch
+    say("cache write", ring, cap, pos0, n)
+    rng = np.random.default_rng(9)
+    Hkv, D = 2, 512
+    k = randn_bf16_bits(rng, (n, Hkv, D))
+    v = randn_bf16_bits(rng, (n, Hkv, D))
+    k0 = randn_bf16_bits(rng, (Hkv, cap, D))
+    v0 = randn_bf16_bits(rng, (Hkv, cap, D))
+    kc, vc = up(k0), up(v0)
+    ga.attn_cache_write(kc, vc, up(k), up(v), pos0, n, Hkv, D, cap, ring)
+    gk, gv = down(kc), down(vc)
+    # expected: slot i holds the chunk row of its position, else unchanged
+    want_k, want_v = k0.copy(), v0.copy()
+    sp = attn_ref.slot_positions(pos0 + n - 1, cap, ring)
+    for i in range(cap):
+        r = sp[i] - pos0
+        if 0 <= r < n:
+            want_k[:, i] = k[r]
+            want_v[:, i] = v[r]
+    assert np.array_equal(gk, want_k) and np.array_equal(gv, want_v)

@@ -4,8 +4,8 @@
     chunk partials for decode, KB-block online softmax for prefill) passes
     attn_ref.check with 0 fails.
   * Controls (planted mistakes, after the pages' practice of controls that
-    "each drop one rounding point" and must be "red as planted", TensorFold PR
-    #1183, receipt): P left unrounded, the wrong key block, P rounded against
+    each remove one rounding point and must fail, TensorFold PR #1183,
+    receipt): P left unrounded, the wrong key block, P rounded against
     the final maximum, bf16 P in decode, a window one key too wide -- each one
     is refused by the check.
   * Planted mistakes inside the oracle itself (a dropped scale, a wrong ring
