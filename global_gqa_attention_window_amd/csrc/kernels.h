@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/gqa_attn.h"
+
 size_t decode_workspace_bytes(int S, int Hq, int D, int cap);
 
 hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* kc,

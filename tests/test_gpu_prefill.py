@@ -1,0 +1,154 @@
+"""GPU parity of attn_cache_write + attn_prefill against the CPU oracle.
+
+Prompt rows are fed chunk by chunk (cache write, then attention) exactly as
+the benchmark feeds them.  The full-size workloads are checked on sampled rows
+(every head, every d) computed by the oracle one row batch at a time; the
+small cases are checked on every output.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import run_prefill, say
+from oracle import attn_ref
+from oracle.contract import P_BF16, P_BF16X2, key_block
+from synthetic.gen import WORKLOADS, f32_to_bf16_bits, prefill_inputs, randn_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ga():
+    import global_gqa_attention_window_amd as ga
+    return ga
+
+
+def _check(tag, got, ref):
+    res = attn_ref.check(got, ref["o"], ref["r"])
+    say(tag, {k: res[k] for k in ("n", "fails", "max_steps_out", "mean_rel_err", "bit_equal")})
+    assert res["ok"], (tag, res)
+
+
+def _sample_rows(n, chunk, rng, n_random=96):
+    rows = set(range(0, min(n, chunk)))                 # the first chunk whole
+    mid = (n // chunk // 2) * chunk
+    rows |= set(range(mid, min(n, mid + chunk)))        # a middle chunk whole
+    rows |= set(range(max(0, n - 16), n))               # the last rows
+    rows |= set(int(x) for x in rng.integers(0, n, n_random))
+    return np.array(sorted(rows))
+
+
+def test_prefill_sliding_8k_full(ga):
+    w = WORKLOADS["prefill_sliding_8k"]
+    say("prefill workload", w.name)
+    q, k, v = prefill_inputs(w)
+    got, _ = run_prefill(ga, q, k, v, w.Hkv, w.cap, w.ring, w.window, w.scale,
+                         w.p_mode, w.chunk)
+    rows = _sample_rows(w.n_rows, w.chunk, np.random.default_rng(1))
+    ref = attn_ref.prefill(q, k, v, 0, w.Hkv, w.window, w.scale, w.p_mode,
+                           key_block(w.D, w.p_mode), rows=rows)
+    _check(w.name, got[rows], ref)
+
+
+def test_prefill_global_32k_full(ga):
+    w = WORKLOADS["prefill_global_32k"]
+    say("prefill workload", w.name)
+    q, k, v = prefill_inputs(w)
+    got, _ = run_prefill(ga, q, k, v, w.Hkv, w.cap, w.ring, w.window, w.scale,
+                         w.p_mode, w.chunk)
+    rng = np.random.default_rng(2)
+    rows = np.array(sorted(set(range(0, 40)) | set(range(16384, 16400)) |
+                           set(range(w.n_rows - 24, w.n_rows)) |
+                           set(int(x) for x in rng.integers(0, w.n_rows, 40))))
+    ref = attn_ref.prefill(q, k, v, 0, w.Hkv, w.window, w.scale, w.p_mode,
+                           key_block(w.D, w.p_mode), rows=rows, row_batch=32)
+    _check(w.name, got[rows], ref)
+
+
+@pytest.mark.parametrize("D,Hq,Hkv,ring,cap,window,chunk,n,pos0,p_mode", [
+    (256, 32, 4, 1, 1152, 1024, 128, 640, 0, P_BF16),       # sliding layer, wraps
+    (256, 8, 1, 1, 200, 150, 37, 300, 0, P_BF16),           # ragged chunks
+    (256, 16, 2, 0, 700, 0, 100, 333, 200, P_BF16X2),       # pos0 > 0, ragged tile
+    (512, 32, 2, 0, 1500, 0, 512, 1100, 0, P_BF16X2),       # global layer
+    (512, 16, 1, 0, 900, 0, 64, 250, 17, P_BF16),
+    (512, 4, 2, 1, 300, 100, 50, 400, 0, P_BF16X2),         # G = 2: idle waves
+    (256, 6, 2, 0, 200, 5, 16, 100, 0, P_BF16),             # G = 3, tiny window
+    (256, 2, 2, 1, 64, 1, 16, 130, 0, P_BF16X2),            # G = 1, window of 1
+    (512, 16, 1, 1, 96, 33, 64, 200, 0, P_BF16),            # ring < block span
+])
+def test_prefill_shapes(ga, D, Hq, Hkv, ring, cap, window, chunk, n, pos0, p_mode):
+    say("prefill shape", D, Hq, Hkv, ring, cap, window, chunk, n, pos0, p_mode)
+    rng = np.random.default_rng(D + Hq + cap + n)
+    q = randn_bf16_bits(rng, (n, Hq, D))
+    k = randn_bf16_bits(rng, (pos0 + n, Hkv, D))
+    v = randn_bf16_bits(rng, (pos0 + n, Hkv, D))
+    scale = 1 / np.sqrt(D)
+    if pos0:
+        # earlier positions are already in the cache
+        import torch
+        from gpu_util import up, DEV
+        kc = torch.zeros((Hkv, cap, D), dtype=torch.int16, device=DEV)
+        vc = torch.zeros_like(kc)
+        ga.attn_cache_write(kc, vc, up(k[:pos0]), up(v[:pos0]), 0, pos0, Hkv, D, cap, ring)
+        caches = (kc, vc)
+    else:
+        caches = None
+    got, _ = run_prefill(ga, q, k, v, Hkv, cap, ring, window, scale, p_mode, chunk,
+                         pos0=pos0, caches=caches)
+    ref = attn_ref.prefill(q, k, v, pos0, Hkv, window, scale, p_mode, key_block(D, p_mode))
+    _check(f"shape D={D} G={Hq // Hkv} ring={ring} W={window} chunk={chunk}", got, ref)
+
+
+def test_prefill_nan_in_unwritten_slots(ga):
+    """Slots never written (NaN) and keys past the tile stay out of the products."""
+    import torch
+    from gpu_util import DEV
+    say("prefill NaN poison")
+    rng = np.random.default_rng(11)
+    D, Hq, Hkv, n, cap, chunk = 512, 16, 1, 200, 256, 72
+    q = randn_bf16_bits(rng, (n, Hq, D))
+    k = randn_bf16_bits(rng, (n, Hkv, D))
+    v = randn_bf16_bits(rng, (n, Hkv, D))
+    kc = torch.full((Hkv, cap, D), 0x7FC0, dtype=torch.int16, device=DEV)
+    vc = torch.full((Hkv, cap, D), 0x7FC0, dtype=torch.int16, device=DEV)
+    got, _ = run_prefill(ga, q, k, v, Hkv, cap, 0, 0, 0.05, P_BF16, chunk, caches=(kc, vc))
+    assert not np.any(((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0))
+    ref = attn_ref.prefill(q, k, v, 0, Hkv, 0, 0.05, P_BF16, key_block(D, P_BF16))
+    _check("nan poison", got, ref)
+
+
+def test_prefill_dominating_key_window_edge(ga):
+    say("prefill dominating key")
+    rng = np.random.default_rng(12)
+    D, Hq, Hkv, n, W, cap = 256, 8, 1, 96, 40, 96
+    q = randn_bf16_bits(rng, (n, Hq, D))
+    q[:] = q[:, :1]                                     # every head the same query
+    k = f32_to_bf16_bits((rng.standard_normal((n, Hkv, D)) * 0.02).astype(np.float32))
+    v = randn_bf16_bits(rng, (n, Hkv, D))
+    i = 80
+    qf = (q[i, 0].astype(np.uint32) << 16).view(np.float32)
+    k[i - W + 1, 0] = f32_to_bf16_bits(8 * qf)          # at the edge: must win
+    got, _ = run_prefill(ga, q, k, v, Hkv, cap, 1, W, 1.0, P_BF16, 32)
+    assert np.all(got[i] == v[i - W + 1, 0][None, :])
+    k2 = k.copy()
+    k2[i - W + 1, 0] = k[0, 0]
+    k2[i - W, 0] = f32_to_bf16_bits(8 * qf)             # one outside: never seen
+    got2, _ = run_prefill(ga, q, k2, v, Hkv, cap, 1, W, 1.0, P_BF16, 32)
+    assert not np.all(got2[i] == v[i - W, 0][None, :])
+    ref = attn_ref.prefill(q, k2, v, 0, Hkv, W, 1.0, P_BF16, key_block(D, P_BF16))
+    _check("dominating", got2, ref)
+
+
+@pytest.mark.parametrize("D,p_mode", [(256, P_BF16), (512, P_BF16X2)])
+def test_prefill_bits_independent_of_chunking(ga, D, p_mode):
+    """Blocks sit on absolute positions, so a row's bits do not depend on how
+    the prompt is cut into chunks, nor on repeating the run."""
+    say("prefill chunking invariance", D)
+    rng = np.random.default_rng(13)
+    Hq, Hkv, n, cap = 16, 2, 512, 512
+    q = randn_bf16_bits(rng, (n, Hq, D))
+    k = randn_bf16_bits(rng, (n, Hkv, D))
+    v = randn_bf16_bits(rng, (n, Hkv, D))
+    outs = [run_prefill(ga, q, k, v, Hkv, cap, 0, 0, 0.04, p_mode, ch)[0]
+            for ch in (512, 128, 48, 512)]
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
