@@ -1,0 +1,211 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = the whole path over one synthetic prompt of the global-layer
+workload: a 32768-token causal prompt (32 query heads over 2 KV heads, head
+dim 512, P kept as two bf16 halves) fed in 64 chunks of 512 rows, each chunk
+a cache write then prompt attention; then one decode row over a 262144-key
+linear cache with the same heads.  Inputs are resident in HBM before timing.
+
+Prints one JSON line: whole-step tokens/s (prompt tokens + the decode token),
+the prefill kernel against the bf16 matrix-core roofline (duration from HIP
+events recorded on the launch stream around every prefill launch), the decode
+kernels against HBM bandwidth, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attn HBM GB/s & prefill tokens/s (8k/32k) vs MI355X roofline"
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=24,
+                    help="prompt rows of the oracle's timed sample")
+    return ap.parse_args()
+
+
+def causal_pairs(n_rows: int, window: int) -> int:
+    """Attended (row, key) pairs of a prompt of n_rows at positions 0.."""
+    if window <= 0:
+        return n_rows * (n_rows + 1) // 2
+    w = min(window, n_rows)
+    return w * (w + 1) // 2 + (n_rows - w) * window
+
+
+def traffic_from_profile(kernel_src: str):
+    """HBM bytes per launch from a committed --pmc summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "prefill_global_32k_pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not (m_sha and m_b):
+        return None
+    sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
+    return float(m_b.group(1)) if sha == m_sha.group(1) else None
+
+
+def cpu_baseline(q, k, v, w, n_rows_sample: int):
+    """The oracle as it stands, on prompt rows spread evenly over the prompt
+    (per-row cost grows with position, so an even spread has the prompt's
+    mean cost), every head; tokens/s = rows / seconds."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attn_ref
+    from oracle.contract import key_block
+
+    n = w.n_rows
+    rows = np.linspace(n // (2 * n_rows_sample), n - 1, n_rows_sample).astype(np.int64)
+    t0 = time.perf_counter()
+    attn_ref.prefill(q, k, v, 0, w.Hkv, w.window, w.scale, w.p_mode,
+                     key_block(w.D, w.p_mode), rows=rows, row_batch=8)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(n_rows_sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_rows_sample} prompt rows evenly spread over positions 0..{n - 1} "
+                      f"of the 32768-token prompt, all 32 heads, float64 NumPy; "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import global_gqa_attention_window_amd as ga
+    from synthetic.gen import WORKLOADS, prefill_inputs, randn_bf16_bits
+
+    w = WORKLOADS["prefill_global_32k"]
+    dev = torch.device("cuda:0")
+    n, ch, Hq, Hkv, D = w.n_rows, w.chunk, w.Hq, w.Hkv, w.D
+    dcap, dpos = w.extra["decode_cap"], w.extra["decode_pos"]
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    q_np, k_np, v_np = prefill_inputs(w)
+    q, k, v = up(q_np), up(k_np), up(v_np)
+    rng = np.random.default_rng(w.extra["decode_seed"])
+    dq = up(randn_bf16_bits(rng, (1, Hq, D)))
+    dk = up(randn_bf16_bits(rng, (1, Hkv, dcap, D)))
+    dv = up(randn_bf16_bits(rng, (1, Hkv, dcap, D)))
+    dpos_t = torch.tensor([dpos], dtype=torch.int32, device=dev)
+    dout = torch.empty((1, Hq, D), dtype=torch.int16, device=dev)
+    ws = torch.empty(ga.attn_decode_workspace_bytes(1, Hq, D, dcap), dtype=torch.uint8,
+                     device=dev)
+    kc = torch.zeros((Hkv, w.cap, D), dtype=torch.int16, device=dev)
+    vc = torch.zeros_like(kc)
+    out = torch.empty((n, Hq, D), dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()
+
+    n_chunks = (n + ch - 1) // ch
+    ev_pf = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n_chunks)]
+    ev_dec = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+    def step(record: bool):
+        for i, r0 in enumerate(range(0, n, ch)):
+            m = min(ch, n - r0)
+            ga.attn_cache_write(kc, vc, k[r0:r0 + m], v[r0:r0 + m], r0, m, Hkv, D,
+                                w.cap, w.ring)
+            if record:
+                ev_pf[i][0].record()
+            ga.attn_prefill(out[r0:r0 + m], q[r0:r0 + m], kc, vc, r0, m, Hq, Hkv, D,
+                            w.cap, w.ring, w.window, w.scale, w.p_mode)
+            if record:
+                ev_pf[i][1].record()
+        if record:
+            ev_dec[0].record()
+        ga.attn_decode(dout, dq, dk, dv, dpos_t, 1, Hq, Hkv, D, dcap, 0, 0, w.scale, ws)
+        if record:
+            ev_dec[1].record()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    pf_ms, dec_ms = 0.0, 0.0
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+        torch.cuda.synchronize()
+        pf_ms += sum(a.elapsed_time(b) for a, b in ev_pf)
+        dec_ms += ev_dec[0].elapsed_time(ev_dec[1])
+    wall = time.perf_counter() - t0
+    torch.cuda.synchronize()
+
+    ms_step = wall * 1e3 / args.steps
+    tokens = n + 1
+    pf_launch_ms = pf_ms / (args.steps * n_chunks)
+    dec_us = dec_ms * 1e3 / args.steps
+
+    flops_prompt = causal_pairs(n, w.window) * Hq * 4 * D        # algorithmic
+    flops_launch = flops_prompt / n_chunks
+    pf_tflops = flops_launch / (pf_launch_ms * 1e-3) / 1e12
+    src = os.path.join(ROOT, "global_gqa_attention_window_amd", "csrc", "prefill.hip")
+    traffic = traffic_from_profile(src)
+    dec_bytes = 2 * Hkv * dcap * D * 2 + 2 * Hq * D * 2           # K+V read, q, out
+    dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "global_layer_prompt_32k_then_decode_262144",
+                   "prompt_tokens": n, "chunk_rows": ch, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": D, "p_mode": "bf16x2", "window": 0,
+                   "decode_cache_keys": dcap, "seed": w.seed},
+        "roofline": {"kernel": "prefill_kernel<512,bf16x2>", "bound": "mfma",
+                     "achieved": round(pf_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pf_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "launch_ms": round(pf_launch_ms, 4),
+                     "flops_per_launch": flops_launch},
+        "prefill": {"tokens_per_s_kernels": round(n / (pf_ms / args.steps * 1e-3), 1),
+                    "kernel_ms_per_prompt": round(pf_ms / args.steps, 3)},
+        "decode": {"us": round(dec_us, 2), "GB/s": round(dec_gbs, 1),
+                   "frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4), "bytes": dec_bytes},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, w, args.cpu_rows)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
