@@ -50,6 +50,15 @@ ATTN_DEV f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
 
 ATTN_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 16 bytes per lane from global memory straight into LDS (global_load_lds
+// dwordx4): lane i writes lds_base + 16 i; lds_base must be wave-uniform.
+// The host compilation pass sees no body (the builtin exists only on gfx950).
+#if defined(__HIP_DEVICE_COMPILE__)
+#define ATTN_DMA16(src, lds_base) __builtin_amdgcn_global_load_lds((src), (lds_base), 16, 0, 0)
+#else
+#define ATTN_DMA16(src, lds_base) ((void)(src), (void)(lds_base))
+#endif
+
 // butterfly over the four lanes l, l^16, l^32, l^48 (same l % 16)
 ATTN_DEV float xmax4(float x) {
     x = fmaxf(x, __shfl_xor(x, 16));

@@ -58,11 +58,13 @@ void decode_partial_kernel(const uint16_t* __restrict__ q,
                            const int32_t* __restrict__ pos,
                            float* __restrict__ part_acc,
                            float* __restrict__ part_ml,
-                           int Hq, int Hkv, int G, int cap, int nch,
+                           int Hq, int Hkv, int G, int cap, int nrun, int cpr,
                            int ring, int window, float c) {
-    constexpr int QST = D / 32;     // 32-wide reduction steps of Q.K
-    constexpr int SPANS = D / 128;  // 128-wide d spans of the accumulator
-    const int chunk = blockIdx.x;
+    constexpr int QST = D / 32;       // 32-wide reduction steps of Q.K
+    constexpr int SPANS = D / 128;    // 128-wide d spans of the accumulator
+    constexpr int LPR = D / 8;        // lanes that move one K row per DMA
+    constexpr int RPD = 64 / LPR;     // K rows per DMA instruction
+    const int run = blockIdx.x;
     const int g = blockIdx.y;
     const int s = blockIdx.z;
     const int lane = threadIdx.x;
@@ -70,15 +72,45 @@ void decode_partial_kernel(const uint16_t* __restrict__ q,
     const int grp = lane >> 4;
     const int t = pos[s];
 
+    // K tiles land here by direct global->LDS loads, two stages
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2][TILE * D];
+
     const size_t head_base = ((size_t)s * Hkv + g) * (size_t)cap;
     const uint16_t* K = kc + head_base * D;
     const uint16_t* V = vc + head_base * D;
+    const int h0 = g * G;
+    const size_t pbase = ((size_t)s * Hq + h0) * (size_t)nrun + run;
+    const int slot0 = run * cpr * CHUNK;
+    const int nslot = min(cpr * CHUNK, cap - slot0);
+    const int ntile = (nslot + TILE - 1) / TILE;
+
+    // attended tiles of this run: [tt_lo, tt_hi]; a run with none writes an
+    // empty partial (m = -inf, l = 0) that the merge skips
+    int tt_lo = 0x7FFFFFFF, tt_hi = -1;
+    for (int tb = 0; tb < ntile; tb += 16) {
+        bool mine = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            mine |= slot_attended(slot0 + (tb + lane / 4) * TILE + 4 * (lane & 3) + i, t, cap, ring, window);
+        const uint64_t bal = __ballot(mine);     // lane covers tile tb + lane / 4
+        if (bal != 0) {
+            tt_lo = min(tt_lo, tb + __builtin_ctzll(bal) / 4);
+            tt_hi = tb + (63 - __builtin_clzll(bal)) / 4;
+        }
+    }
+    if (tt_hi < 0) {
+        if (col < G && grp == 0) {
+            part_ml[2 * (pbase + (size_t)col * nrun) + 0] = -INFINITY;
+            part_ml[2 * (pbase + (size_t)col * nrun) + 1] = 0.f;
+        }
+        return;
+    }
 
     // Q^T operand: lane holds Q[head col][32 st + 8 grp .. +7]
     u32x4 qreg[QST];
     {
         const bool hv = col < G;
-        const uint16_t* qrow = q + ((size_t)s * Hq + (size_t)g * G + (hv ? col : 0)) * D;
+        const uint16_t* qrow = q + ((size_t)s * Hq + h0 + (hv ? col : 0)) * D;
 #pragma unroll
         for (int st = 0; st < QST; ++st) {
             u32x4 z = {0u, 0u, 0u, 0u};
@@ -92,61 +124,80 @@ void decode_partial_kernel(const uint16_t* __restrict__ q,
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[sp][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    const int slot0 = chunk * CHUNK;
-
-    for (int tt = 0; tt < CHUNK / TILE; ++tt) {
-        const int sb = slot0 + tt * TILE;
-        // attended keys of this tile: lane's K row (sb + col) and its four
-        // score keys (sb + 4 grp + i)
-        const bool krow_ok = slot_attended(sb + col, t, cap, ring, window);
-        if (!__any(krow_ok)) continue;   // uniform: nothing attended here
-
-        u32x4 kreg[QST];
-        const uint16_t* krow = K + (size_t)(sb + col) * D + 8 * grp;
+    // K tile: each DMA instruction moves 1 KiB of whole rows (one row at
+    // D=512, two at 256).  16-byte chunk c of row r sits at chunk c ^ (r & 7)
+    // of its LDS row, so the eight lanes of one LDS read phase (eight rows,
+    // same chunk) hit eight different bank groups.  The slot is clamped in
+    // range; a key that is not attended is masked out of the scores.
+    auto load_k = [&](int sb, int stage) {
 #pragma unroll
-        for (int st = 0; st < QST; ++st) {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            kreg[st] = krow_ok ? ld16(krow + 32 * st) : z;
+        for (int i = 0; i < TILE / RPD; ++i) {
+            const int row = i * RPD + lane / LPR;
+            const int slot = min(sb + row, cap - 1);
+            const int chunk = (lane % LPR) ^ (row & 7);
+            ATTN_DMA16(K + (size_t)slot * D + chunk * 8, &ks[stage][i * RPD * D]);
         }
-        // V rows (sb + 4 grp + r), d = 128 sp + 8 col .. +7
-        bool vok[4];
-        u32x4 vreg[4][SPANS];
+    };
+    // V rows (sb + 4 grp + r), d = 128 sp + 8 col .. +7: sixteen lanes read
+    // 256 contiguous bytes of one row per load
+    u32x4 vcur[4][SPANS];
+    u32x4 vnxt[4][SPANS];
+    auto load_v = [&](int sb, u32x4 (&dst)[4][SPANS]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            vok[r] = slot_attended(sb + 4 * grp + r, t, cap, ring, window);
-            const uint16_t* vrow = V + (size_t)(sb + 4 * grp + r) * D + 8 * col;
+            const int slot = min(sb + 4 * grp + r, cap - 1);
+            const uint16_t* vrow = V + (size_t)slot * D + 8 * col;
 #pragma unroll
-            for (int sp = 0; sp < SPANS; ++sp) {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                vreg[r][sp] = vok[r] ? ld16(vrow + 128 * sp) : z;
-            }
+            for (int sp = 0; sp < SPANS; ++sp) dst[r][sp] = ld16(vrow + 128 * sp);
         }
+    };
 
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    load_k(slot0 + tt_lo * TILE, 0);
+    load_v(slot0 + tt_lo * TILE, vcur);
+    for (int tt = tt_lo; tt <= tt_hi; ++tt) {
+        const int stage = (tt - tt_lo) & 1;
+        const int sb = slot0 + tt * TILE;
+        // K(tt) in LDS and V(tt) in registers have landed
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tt < tt_hi) load_k(sb + TILE, stage ^ 1);
+
+        const uint16_t* kt = &ks[stage][0];
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < QST; ++st) sc = mfma_bf16_16x16x32(kreg[st], qreg[st], sc);
+        for (int st = 0; st < QST; ++st)
+            sc = mfma_bf16_16x16x32(ld16(kt + col * D + 8 * ((4 * st + grp) ^ (col & 7))), qreg[st], sc);
 
         float tv[4];
+        uint32_t vmask[4], vsel[4];
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            tv[i] = vok[i] ? sc[i] * c : -INFINITY;
+            const bool ok = slot_attended(sb + 4 * grp + i, t, cap, ring, window);
+            tv[i] = ok ? sc[i] * c : -INFINITY;
             mx = fmaxf(mx, tv[i]);
+            // bf16 -> fp32 of V with unattended keys forced to +0 (a NaN
+            // there must not meet its zero probability)
+            vmask[i] = ok ? 0xFFFF0000u : 0u;
+            vsel[i] = ok ? 0x01000C0Cu : 0x0C0C0C0Cu;
         }
         mx = xmax4(mx);
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);   // 0 when m_run = -inf
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);   // 0 when m_run = -inf
         float pv[4];
         float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            pv[i] = vok[i] ? fast_exp2(tv[i] - m_new) : 0.f;
+            pv[i] = fast_exp2(tv[i] - m_use);              // 0 for masked keys
             psum += pv[i];
         }
         l_run = l_run * alpha + psum;
         m_run = m_new;
+        if (tt < tt_hi) load_v(sb + TILE, vnxt);      // in flight during P.V
         if (__any(alpha != 1.f)) {
 #pragma unroll
             for (int sp = 0; sp < SPANS; ++sp)
@@ -157,23 +208,32 @@ void decode_partial_kernel(const uint16_t* __restrict__ q,
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
             for (int sp = 0; sp < SPANS; ++sp) {
-                const u32x4 w = vreg[r][sp];
-                acc[sp][0] = mfma_f32_16x16x4(bf16lo_to_f32(w.x), pv[r], acc[sp][0]);
-                acc[sp][1] = mfma_f32_16x16x4(bf16hi_to_f32(w.x), pv[r], acc[sp][1]);
-                acc[sp][2] = mfma_f32_16x16x4(bf16lo_to_f32(w.y), pv[r], acc[sp][2]);
-                acc[sp][3] = mfma_f32_16x16x4(bf16hi_to_f32(w.y), pv[r], acc[sp][3]);
-                acc[sp][4] = mfma_f32_16x16x4(bf16lo_to_f32(w.z), pv[r], acc[sp][4]);
-                acc[sp][5] = mfma_f32_16x16x4(bf16hi_to_f32(w.z), pv[r], acc[sp][5]);
-                acc[sp][6] = mfma_f32_16x16x4(bf16lo_to_f32(w.w), pv[r], acc[sp][6]);
-                acc[sp][7] = mfma_f32_16x16x4(bf16hi_to_f32(w.w), pv[r], acc[sp][7]);
+                const u32x4 w = vcur[r][sp];
+                const float p = pv[r];
+                const uint32_t sl = vsel[r], mk = vmask[r];
+#define LO(x) __uint_as_float(__builtin_amdgcn_perm(0u, (x), sl))
+#define HI(x) __uint_as_float((x) & mk)
+                acc[sp][0] = mfma_f32_16x16x4(LO(w.x), p, acc[sp][0]);
+                acc[sp][1] = mfma_f32_16x16x4(HI(w.x), p, acc[sp][1]);
+                acc[sp][2] = mfma_f32_16x16x4(LO(w.y), p, acc[sp][2]);
+                acc[sp][3] = mfma_f32_16x16x4(HI(w.y), p, acc[sp][3]);
+                acc[sp][4] = mfma_f32_16x16x4(LO(w.z), p, acc[sp][4]);
+                acc[sp][5] = mfma_f32_16x16x4(HI(w.z), p, acc[sp][5]);
+                acc[sp][6] = mfma_f32_16x16x4(LO(w.w), p, acc[sp][6]);
+                acc[sp][7] = mfma_f32_16x16x4(HI(w.w), p, acc[sp][7]);
+#undef LO
+#undef HI
             }
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int sp = 0; sp < SPANS; ++sp) vcur[r][sp] = vnxt[r][sp];
     }
 
     const float l_tot = xsum4(l_run);
     if (col >= G) return;
-    const int h = g * G + col;
-    const size_t pidx = ((size_t)s * Hq + h) * (size_t)nch + chunk;
+    const size_t pidx = pbase + (size_t)col * nrun;
     if (grp == 0) {
         part_ml[2 * pidx + 0] = m_run;
         part_ml[2 * pidx + 1] = l_tot;
@@ -193,42 +253,86 @@ void decode_partial_kernel(const uint16_t* __restrict__ q,
     }
 }
 
-// Merge of chunk partials in ascending chunk order: M = max over live chunks,
-// out = bf16(sum e^(m_c - M) acc_c / sum e^(m_c - M) l_c).  A chunk with no
-// attended key (m = -inf) is skipped, never multiplied.  Block: 64 threads,
-// four consecutive d each (256 d); grid (Hq, S, D / 256).
+// Merge of chunk partials in ascending chunk order.  A block of MW waves
+// serves one (stream, head) and 256 d (four per lane); wave w takes the
+// contiguous chunk range [w nch / MW, (w + 1) nch / MW) in ascending order,
+// then the waves' sums are added in ascending wave order.  M is the largest
+// chunk maximum; chunks with no attended key (m = -inf) are skipped, never
+// multiplied; out = bf16(sum e^(m_c - M) acc_c / sum e^(m_c - M) l_c).
+constexpr int MW = 16;
+
 template <int D>
-__global__ __launch_bounds__(64)
+__global__ __launch_bounds__(64 * MW)
 void decode_merge_kernel(uint16_t* __restrict__ out,
                          const float* __restrict__ part_acc,
                          const float* __restrict__ part_ml,
                          int Hq, int nch) {
-    const int h = blockIdx.x;
-    const int s = blockIdx.y;
-    const int d0 = blockIdx.z * 256 + threadIdx.x * 4;
-    const size_t base = ((size_t)s * Hq + h) * (size_t)nch;
+    __shared__ float s_max[MW];
+    __shared__ float s_l[MW];
+    __shared__ f32x4 s_o[MW][64];
+    const int sh = blockIdx.x;                 // s * Hq + h
+    const int d0 = blockIdx.y * 256 + (threadIdx.x & 63) * 4;
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const size_t base = (size_t)sh * (size_t)nch;
     const float2* ml = reinterpret_cast<const float2*>(part_ml) + base;
+    const int c0 = (int)((long long)w * nch / MW);
+    const int c1 = (int)((long long)(w + 1) * nch / MW);
 
+    float mw = -INFINITY;
+    for (int cidx = c0 + lane; cidx < c1; cidx += 64) mw = fmaxf(mw, ml[cidx].x);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mw = fmaxf(mw, __shfl_xor(mw, o));
+    if (lane == 0) s_max[w] = mw;
+    __syncthreads();
     float M = -INFINITY;
-    for (int cidx = 0; cidx < nch; ++cidx) M = fmaxf(M, ml[cidx].x);
+#pragma unroll
+    for (int i = 0; i < MW; ++i) M = fmaxf(M, s_max[i]);
 
     float L = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
-        for (int cidx = 0; cidx < nch; ++cidx) {
+        int cidx = c0;
+        for (; cidx + 4 <= c1; cidx += 4) {
+            f32x4 a[4];
+            float2 e[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                e[u] = ml[cidx + u];
+                a[u] = *reinterpret_cast<const f32x4*>(part_acc + (base + cidx + u) * D + d0);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (e[u].x == -INFINITY) continue;
+                const float wt = fast_exp2(e[u].x - M);
+                L += wt * e[u].y;
+                o += wt * a[u];
+            }
+        }
+        for (; cidx < c1; ++cidx) {
             const float2 e = ml[cidx];
             if (e.x == -INFINITY) continue;
-            const float w = fast_exp2(e.x - M);
-            L += w * e.y;
-            const f32x4 a = *reinterpret_cast<const f32x4*>(part_acc + (base + cidx) * D + d0);
-            o += w * a;
+            const float wt = fast_exp2(e.x - M);
+            L += wt * e.y;
+            o += wt * *reinterpret_cast<const f32x4*>(part_acc + (base + cidx) * D + d0);
         }
+    }
+    s_o[w][lane] = o;
+    if (lane == 0) s_l[w] = L;
+    __syncthreads();
+    if (w != 0) return;
+    float Lt = 0.f;
+    f32x4 ot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < MW; ++i) {
+        Lt += s_l[i];
+        ot += s_o[i][lane];
     }
     uint32_t b[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = (L != 0.f || L != L) ? f32_to_bf16_bits(o[i] / L) : 0u;
+    for (int i = 0; i < 4; ++i) b[i] = (Lt != 0.f || Lt != Lt) ? f32_to_bf16_bits(ot[i] / Lt) : 0u;
     u32x2 packed = {pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
-    *reinterpret_cast<u32x2*>(out + ((size_t)s * Hq + h) * D + d0) = packed;
+    *reinterpret_cast<u32x2*>(out + (size_t)sh * D + d0) = packed;
 }
 
 }  // namespace
@@ -243,20 +347,25 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                          int Hkv, int D, int cap, int ring, int window,
                          float scale, void* ws, hipStream_t stream) {
     const int nch = (cap + CHUNK - 1) / CHUNK;
+    // a workgroup carries its softmax over a run of consecutive chunks; runs
+    // of two when there are chunks for more than one wave per SIMD
+    const long long waves = (long long)nch * Hkv * S;
+    const int cpr = waves > 1536 ? 2 : 1;
+    const int nrun = (nch + cpr - 1) / cpr;
     const int G = Hq / Hkv;
     float* part_acc = reinterpret_cast<float*>(ws);
-    float* part_ml = part_acc + (size_t)S * Hq * nch * D;
+    float* part_ml = part_acc + (size_t)S * Hq * nrun * D;
     const float c = scale * ATTN_LOG2E;
-    dim3 g1(nch, Hkv, S);
-    dim3 g2(Hq, S, D / 256);
+    dim3 g1(nrun, Hkv, S);
+    dim3 g2(S * Hq, D / 256);
     if (D == 256) {
         decode_partial_kernel<256><<<g1, 64, 0, stream>>>(q, kc, vc, pos, part_acc, part_ml,
-                                                          Hq, Hkv, G, cap, nch, ring, window, c);
-        decode_merge_kernel<256><<<g2, 64, 0, stream>>>(out, part_acc, part_ml, Hq, nch);
+                                                          Hq, Hkv, G, cap, nrun, cpr, ring, window, c);
+        decode_merge_kernel<256><<<g2, 64 * MW, 0, stream>>>(out, part_acc, part_ml, Hq, nrun);
     } else {
         decode_partial_kernel<512><<<g1, 64, 0, stream>>>(q, kc, vc, pos, part_acc, part_ml,
-                                                          Hq, Hkv, G, cap, nch, ring, window, c);
-        decode_merge_kernel<512><<<g2, 64, 0, stream>>>(out, part_acc, part_ml, Hq, nch);
+                                                          Hq, Hkv, G, cap, nrun, cpr, ring, window, c);
+        decode_merge_kernel<512><<<g2, 64 * MW, 0, stream>>>(out, part_acc, part_ml, Hq, nrun);
     }
     return hipGetLastError();
 }
