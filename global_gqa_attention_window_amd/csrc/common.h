@@ -40,6 +40,15 @@ ATTN_DEV uint32_t pack_bf16x2(uint32_t lo_bits, uint32_t hi_bits) {
 
 ATTN_DEV bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// two fp32 -> packed bf16 pair (lo, hi) with v_cvt_pk_bf16_f32: round to
+// nearest even, NaN stays NaN
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+ATTN_DEV uint32_t cvt_pk_bf16(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 ATTN_DEV f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
@@ -58,6 +67,23 @@ ATTN_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 #else
 #define ATTN_DMA16(src, lds_base) ((void)(src), (void)(lds_base))
 #endif
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane j points at four consecutive 16-bit elements M[j][0..3]; lane i gets
+// back M[4 k + (i >> 2)][i & 3] for k = 0..3 (measured on gfx950).  Pointing
+// lane j at row kappa(j >> 2), column c0 + 4 (j & 3) of a row-major matrix
+// therefore hands lane i the four rows kappa(0..3) at column c0 + i.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+ATTN_DEV u32x2 lds_read_tr16(const uint16_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
+#else
+    (void)p;
+    return u32x2{0u, 0u};
+#endif
+}
 
 // butterfly over the four lanes l, l^16, l^32, l^48 (same l % 16)
 ATTN_DEV float xmax4(float x) {

@@ -9,24 +9,32 @@
 // over 128-dim slices (the score accumulates 32-wide steps in ascending d, so
 // 128-wide slices add in slice order) and P may be kept as two bf16 halves.
 //
-// MI355X design (v1).  A workgroup of four waves takes one 16-row tile of the
+// MI355X design.  A workgroup of four waves takes one 16-row tile of the
 // chunk and four query heads of one KV group; wave w owns head w: 16 rows x
 // the whole head dim, so its softmax state never leaves the wave.  The four
-// heads share every K/V block, staged once in LDS and double-buffered: while
-// the waves multiply block b, the next block's 16-byte global loads are in
-// flight in registers and land in the other LDS stage after the products.
-//   S^T[key][row] = K . Q^T  v_mfma_f32_16x16x32_bf16, K rows from LDS,
-//                            Q^T resident in registers for the whole walk;
-//   O^T[d][row] += V^T . P^T v_mfma_f32_16x16x32_bf16 with P (or its bf16 hi
-//                            and lo halves, two products) as the B operand;
-//                            V is written to LDS transposed, in a key order
-//                            that matches the lanes' P registers, so each A
-//                            operand is one 16-byte LDS read.
+// heads share every key block: K and V rows land in LDS by direct
+// global->LDS loads (1 KiB of whole rows per instruction, no registers, no
+// VALU), two stages, the next block in flight while the current one is
+// multiplied.  Rows are padded in LDS (K by 16 bytes, V by 32) so that the
+// score reads (eight rows, one 16-byte chunk each) and the transpose reads
+// (four rows, 32 bytes each) fall on distinct banks, and every LDS address
+// is a per-lane base plus a constant offset.  At head dim 256 one DMA
+// instruction moves two 512-byte rows back to back; it takes rows r and
+// r + 8 of a 16-row group, which no read phase uses together, and the
+// padding sits between such pairs.
+//   S^T[key][row] = K . Q^T   v_mfma_f32_16x16x32_bf16: K rows from LDS,
+//                             Q^T resident in registers for the whole walk;
+//   O^T[d][row] += V^T . P^T  v_mfma_f32_16x16x32_bf16 with P (or its bf16
+//                             hi and lo halves, two products) as B; the V^T
+//                             operand comes straight from the row-major V
+//                             block through two transpose reads.
 // Lane l always owns query row l % 16 (the S^T and O^T column), so the row's
 // maximum, rescale and sum stay in its four lanes (l, l^16, l^32, l^48).
 // Key blocks are KB keys aligned to absolute positions; the running maximum
-// moves once per block and p is rounded against it.  Keys of a block outside
-// the tile's attended span [lo, hi] are stored as zeros, never loaded.
+// moves once per block and p is rounded against it.  Key slots of a block
+// outside the tile's attended span [lo, hi] are fetched from a position
+// inside the span instead: their scores are masked, and their V rows are
+// finite, so they add exactly zero (a never-written row is never read).
 #include "common.h"
 #include "kernels.h"
 
@@ -36,6 +44,16 @@ template <int D> struct PrefillCfg;
 template <> struct PrefillCfg<256> { static constexpr int KB = 64; };
 template <> struct PrefillCfg<512> { static constexpr int KB = 32; };
 
+// element offset of block row r in LDS (PADP: padding elements per unit)
+template <int D, int PADP>
+ATTN_DEV constexpr int row_pos(int r) {
+    if constexpr (D == 512) {
+        return r * (D + PADP);
+    } else {
+        return ((r >> 4) * 8 + (r & 7)) * (2 * D + PADP) + ((r >> 3) & 1) * D;
+    }
+}
+
 template <int D, int PM>
 __global__ __launch_bounds__(256)
 void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
@@ -43,21 +61,17 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     int pos0, int n_rows, int Hq, int Hkv, int G, int HG, int cap,
                     int ring, int window, float c) {
     constexpr int KB = PrefillCfg<D>::KB;
-    constexpr int KP = D + 8;                // K row stride in LDS (elements)
-    constexpr int VP = KB + 8;               // V^T row stride in LDS
-    constexpr int K_ELEMS = KB * KP;
-    constexpr int STAGE = K_ELEMS + D * VP;
+    constexpr int KPADP = 8;                 // K padding per row (pair at 256)
+    constexpr int VPADP = 16;                // V padding per row (pair at 256)
+    constexpr int KBLK = row_pos<D, KPADP>(KB);
+    constexpr int VBLK = row_pos<D, VPADP>(KB);
     constexpr int QST = D / 32;              // reduction steps of a score
     constexpr int KT = KB / 16;              // 16-key score tiles per block
     constexpr int KS = KB / 32;              // 32-key steps of P.V per block
     constexpr int DT = D / 16;               // 16-wide d tiles of the output
-    constexpr int VEC_ROW = D / 8;           // 16-byte vectors per cache row
-    constexpr int K_VECS = KB * VEC_ROW / 256;       // per thread
-    constexpr int V_UNITS = (KB / 4) * VEC_ROW / 256; // 4-key units per thread
-    static_assert(K_VECS * 256 == KB * VEC_ROW, "K staging");
-    static_assert(V_UNITS * 256 == (KB / 4) * VEC_ROW, "V staging");
+    constexpr int LPR = D / 8;               // lanes that move one row
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][KBLK + VBLK];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -74,6 +88,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int t_first = pos0 + r0;
     const int t_last = pos0 + r0 + nvalid - 1;
     const int lo_tile = window > 0 ? max(0, t_first - window + 1) : 0;
+    const int lo_last = window > 0 ? max(0, t_last - window + 1) : 0;
     const int hi_tile = t_last;
     const int b_lo = lo_tile / KB;
     const int b_hi = hi_tile / KB;
@@ -96,65 +111,33 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* Kg = kc + (size_t)g * cap * D;
     const uint16_t* Vg = vc + (size_t)g * cap * D;
 
-    u32x4 kst[K_VECS];
-    u32x4 vst[V_UNITS][4];
-
-    auto slot_of = [&](int p) -> size_t { return (size_t)(ring ? p % cap : p); };
-
-    auto gload = [&](int b) {
-        const int p0 = b * KB;
+    // block b -> LDS stage: 2 KB rows (K rows first, then V rows), each DMA
+    // instruction moves 1 KiB: one row at D=512, rows r and r + 8 of a
+    // 16-row group at D=256 (lanes 0..31 and 32..63); wave w issues
+    // instructions [w N, (w + 1) N)
+    constexpr int INSTR = 2 * KB * LPR / 64;
+    constexpr int INSTR_PER_WAVE = INSTR / 4;
+    static_assert(INSTR_PER_WAVE * 4 == INSTR, "DMA split");
+    auto dma_block = [&](int b, int stage) {
 #pragma unroll
-        for (int it = 0; it < K_VECS; ++it) {
-            const int vi = tid + 256 * it;
-            const int key = vi / VEC_ROW;
-            const int dv = vi % VEC_ROW;
-            const int p = p0 + key;
-            u32x4 z = {0u, 0u, 0u, 0u};
-            kst[it] = (p >= lo_tile && p <= hi_tile) ? ld16(Kg + slot_of(p) * D + dv * 8) : z;
-        }
-#pragma unroll
-        for (int u = 0; u < V_UNITS; ++u) {
-            const int ui = tid + 256 * u;
-            const int k4 = ui % (KB / 4);
-            const int dv = ui / (KB / 4);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int p = p0 + 4 * k4 + kk;
-                u32x4 z = {0u, 0u, 0u, 0u};
-                vst[u][kk] = (p >= lo_tile && p <= hi_tile) ? ld16(Vg + slot_of(p) * D + dv * 8) : z;
+        for (int i = 0; i < INSTR_PER_WAVE; ++i) {
+            const int j = wave * INSTR_PER_WAVE + i;     // instruction index
+            const bool is_v = j >= INSTR / 2;            // uniform
+            const int jj = is_v ? j - INSTR / 2 : j;
+            int r0i, r;                                  // first row, this lane's row
+            if constexpr (LPR == 64) {
+                r0i = jj;
+                r = jj;
+            } else {
+                r0i = 16 * (jj >> 3) + (jj & 7);
+                r = r0i + 8 * (lane >> 5);
             }
-        }
-    };
-
-    auto lstore = [&](int stg) {
-        uint16_t* Kl = lds + stg * STAGE;
-        uint16_t* Vl = Kl + K_ELEMS;
-#pragma unroll
-        for (int it = 0; it < K_VECS; ++it) {
-            const int vi = tid + 256 * it;
-            st16(Kl + (vi / VEC_ROW) * KP + (vi % VEC_ROW) * 8, kst[it]);
-        }
-#pragma unroll
-        for (int u = 0; u < V_UNITS; ++u) {
-            const int ui = tid + 256 * u;
-            const int k4 = ui % (KB / 4);
-            const int dv = ui / (KB / 4);
-            // keys 4 k4 .. +3 of the 32-key group k4 / 8 go to the columns
-            // where the P.V step expects them: lane group g' reads columns
-            // 8 g' .. 8 g' + 7 = keys 4 g' .. +3 and 16 + 4 g' .. +3
-            const int k4l = k4 & 7;
-            const int cst = 32 * (k4 >> 3) + (k4l < 4 ? 8 * k4l : 8 * (k4l - 4) + 4);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int w = j >> 1;
-                const int sh = (j & 1) * 16;
-                const uint32_t e0 = (vst[u][0][w] >> sh) & 0xFFFFu;
-                const uint32_t e1 = (vst[u][1][w] >> sh) & 0xFFFFu;
-                const uint32_t e2 = (vst[u][2][w] >> sh) & 0xFFFFu;
-                const uint32_t e3 = (vst[u][3][w] >> sh) & 0xFFFFu;
-                u32x2 pk = {e0 | (e1 << 16), e2 | (e3 << 16)};
-                *reinterpret_cast<u32x2*>(Vl + (dv * 8 + j) * VP + cst) = pk;
-            }
+            const int p = min(max(b * KB + r, lo_tile), hi_tile);
+            const int slot = ring ? p % cap : p;
+            const uint16_t* src = (is_v ? Vg : Kg) + (size_t)slot * D + (lane % LPR) * 8;
+            uint16_t* dst = &lds[stage][is_v ? KBLK + row_pos<D, VPADP>(r0i)
+                                             : row_pos<D, KPADP>(r0i)];
+            ATTN_DMA16(src, dst);
         }
     };
 
@@ -164,27 +147,40 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    gload(b_lo);
-    lstore(0);
-    __syncthreads();
+    // per-lane LDS bases: score reads use K row col of tile kt, transpose
+    // reads V rows 32 ks + 4 grp + (col >> 2) (+16); both tile offsets are
+    // compile-time constants (row_pos is linear in whole 16-row groups)
+    const uint16_t* kbase = &lds[0][0] + row_pos<D, KPADP>(col) + 8 * grp;
+    const uint16_t* vbase = &lds[0][0] + KBLK + row_pos<D, VPADP>(4 * grp + (col >> 2)) + 4 * (col & 3);
+    constexpr int K16 = row_pos<D, KPADP>(16);     // offset of the next 16 rows
+    constexpr int V16 = row_pos<D, VPADP>(16);
 
+    dma_block(b_lo, 0);
     for (int b = b_lo; b <= b_hi; ++b) {
         const int stg = (b - b_lo) & 1;
-        const bool more = b < b_hi;
-        if (more) gload(b + 1);
-        if (head_ok) {
-            const uint16_t* Kl = lds + stg * STAGE;
-            const uint16_t* Vl = Kl + K_ELEMS;
-            const int p0 = b * KB;
-            // scores: tile kt holds keys 16 kt + (0..15) in natural order;
-            // lane has keys 16 kt + 4 grp + i for its row
-            float sv[KT][4];
+        __builtin_amdgcn_s_waitcnt(0);           // this wave's part of block b
+        __syncthreads();                          // every wave's part; stage stg^1 free
+        if (b < b_hi) dma_block(b + 1, stg ^ 1);  // in flight while b is multiplied
+        if (!head_ok) continue;
+        const uint16_t* Kl = kbase + stg * (KBLK + VBLK);
+        const uint16_t* Vl = vbase + stg * (KBLK + VBLK);
+        const int p0 = b * KB;
+        // every row of the tile sees every key of this block
+        const bool interior = p0 >= lo_last && p0 + KB - 1 <= t_first;
+
+        // scores: tile kt holds keys 16 kt + (0..15); lane has keys
+        // 16 kt + 4 grp + i of its row
+        float sv[KT][4];
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                f32x4 a = {0.f, 0.f, 0.f, 0.f};
-                const uint16_t* krow = Kl + (16 * kt + col) * KP + 8 * grp;
+        for (int kt = 0; kt < KT; ++kt) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int st = 0; st < QST; ++st) a = mfma_bf16_16x16x32(ld16(krow + 32 * st), qreg[st], a);
+            for (int st = 0; st < QST; ++st)
+                a = mfma_bf16_16x16x32(ld16(Kl + kt * K16 + 32 * st), qreg[st], a);
+            if (interior) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sv[kt][i] = a[i] * c;
+            } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int p = p0 + 16 * kt + 4 * grp + i;
@@ -192,53 +188,61 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     sv[kt][i] = ok ? a[i] * c : -INFINITY;
                 }
             }
-            float mx = -INFINITY;
+        }
+        float mx = sv[0][0];
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
+        for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[kt][i]);
-            mx = xmax4(mx);
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = fast_exp2(m_run - m_use);
-            float psum = 0.f;
-            u32x4 phi[KS];
-            u32x4 plo[KS];
+            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[kt][i]);
+        mx = xmax4(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float psum = 0.f;
+        // P.V step ks: lane's k-slots (grp, e) are keys 32 ks + 4 grp + e
+        // (e < 4) and 32 ks + 16 + 4 grp + (e - 4), from tiles 2 ks, 2 ks + 1
+        u32x4 phi[KS];
+        u32x4 plo[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                uint32_t hb[8], lb[8];
+        for (int ks = 0; ks < KS; ++ks) {
+            float pe[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int kt = 2 * ks + (e >> 2);
-                    const float p = fast_exp2(sv[kt][e & 3] - m_use);
-                    psum += p;
-                    hb[e] = f32_to_bf16_bits(p);
-                    if (PM == ATTN_P_BF16X2) lb[e] = f32_to_bf16_bits(p - __uint_as_float(hb[e] << 16));
-                }
-                phi[ks] = u32x4{pack_bf16x2(hb[0], hb[1]), pack_bf16x2(hb[2], hb[3]),
-                                pack_bf16x2(hb[4], hb[5]), pack_bf16x2(hb[6], hb[7])};
-                if (PM == ATTN_P_BF16X2)
-                    plo[ks] = u32x4{pack_bf16x2(lb[0], lb[1]), pack_bf16x2(lb[2], lb[3]),
-                                    pack_bf16x2(lb[4], lb[5]), pack_bf16x2(lb[6], lb[7])};
+            for (int e = 0; e < 8; ++e) {
+                pe[e] = fast_exp2(sv[2 * ks + (e >> 2)][e & 3] - m_use);
+                psum += pe[e];
             }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            if (__any(alpha != 1.f)) {
+            uint32_t hw[4];
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-            }
+            for (int u = 0; u < 4; ++u) hw[u] = cvt_pk_bf16(pe[2 * u], pe[2 * u + 1]);
+            phi[ks] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+            if (PM == ATTN_P_BF16X2) {
+                uint32_t lw[4];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const u32x4 a = ld16(Vl + (16 * dt + col) * VP + 32 * ks + 8 * grp);
-                    oacc[dt] = mfma_bf16_16x16x32(a, phi[ks], oacc[dt]);
-                    if (PM == ATTN_P_BF16X2) oacc[dt] = mfma_bf16_16x16x32(a, plo[ks], oacc[dt]);
-                }
+                for (int u = 0; u < 4; ++u)
+                    lw[u] = cvt_pk_bf16(pe[2 * u] - bf16lo_to_f32(hw[u]),
+                                        pe[2 * u + 1] - bf16hi_to_f32(hw[u]));
+                plo[ks] = u32x4{lw[0], lw[1], lw[2], lw[3]};
             }
         }
-        if (more) lstore(stg ^ 1);
-        __syncthreads();
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        }
+        // V^T operand by transpose reads: lane j of a 16-lane group points at
+        // V row (key of k-slot j >> 2), columns 16 dt + 4 (j & 3) .. +3
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const u32x2 x0 = lds_read_tr16(Vl + 2 * ks * V16 + 16 * dt);
+                const u32x2 x1 = lds_read_tr16(Vl + (2 * ks + 1) * V16 + 16 * dt);
+                const u32x4 a = {x0.x, x0.y, x1.x, x1.y};
+                oacc[dt] = mfma_bf16_16x16x32(a, phi[ks], oacc[dt]);
+                if (PM == ATTN_P_BF16X2) oacc[dt] = mfma_bf16_16x16x32(a, plo[ks], oacc[dt]);
+            }
+        }
     }
 
     const float l_tot = xsum4(l_run);
@@ -246,11 +250,8 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     uint16_t* orow = out + ((size_t)(r0 + col) * Hq + h) * D + 4 * grp;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-        uint32_t b0 = f32_to_bf16_bits(oacc[dt][0] / l_tot);
-        uint32_t b1 = f32_to_bf16_bits(oacc[dt][1] / l_tot);
-        uint32_t b2 = f32_to_bf16_bits(oacc[dt][2] / l_tot);
-        uint32_t b3 = f32_to_bf16_bits(oacc[dt][3] / l_tot);
-        u32x2 pk = {pack_bf16x2(b0, b1), pack_bf16x2(b2, b3)};
+        u32x2 pk = {cvt_pk_bf16(oacc[dt][0] / l_tot, oacc[dt][1] / l_tot),
+                    cvt_pk_bf16(oacc[dt][2] / l_tot, oacc[dt][3] / l_tot)};
         *reinterpret_cast<u32x2*>(orow + 16 * dt) = pk;
     }
 }
