@@ -70,8 +70,15 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     constexpr int KS = KB / 32;              // 32-key steps of P.V per block
     constexpr int DT = D / 16;               // 16-wide d tiles of the output
     constexpr int LPR = D / 8;               // lanes that move one row
+    constexpr int INSTR = KB * LPR / 64;     // DMA instructions per K (or V) block
+    constexpr int IPW = INSTR / 4;           // ... per wave
+    static_assert(IPW * 4 == INSTR, "DMA split");
+    constexpr int K16 = row_pos<D, KPADP>(16);     // offset of the next 16 rows
+    constexpr int V16 = row_pos<D, VPADP>(16);
 
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][KBLK + VBLK];
+    // two K stages and two V stages: K runs one block ahead of V
+    __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][KBLK];
+    __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2][VBLK];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -111,33 +118,38 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const uint16_t* Kg = kc + (size_t)g * cap * D;
     const uint16_t* Vg = vc + (size_t)g * cap * D;
 
-    // block b -> LDS stage: 2 KB rows (K rows first, then V rows), each DMA
-    // instruction moves 1 KiB: one row at D=512, rows r and r + 8 of a
-    // 16-row group at D=256 (lanes 0..31 and 32..63); wave w issues
-    // instructions [w N, (w + 1) N)
-    constexpr int INSTR = 2 * KB * LPR / 64;
-    constexpr int INSTR_PER_WAVE = INSTR / 4;
-    static_assert(INSTR_PER_WAVE * 4 == INSTR, "DMA split");
-    auto dma_block = [&](int b, int stage) {
+    // DMA of one K or V block: instruction j (wave w issues [w IPW, (w+1) IPW))
+    // moves 1 KiB: block row j at D=512, rows 16 (j >> 3) + (j & 7) and +8 at
+    // D=256 (lanes 0..31 and 32..63).  A block whose KB positions all lie in
+    // the tile's span and do not wrap the ring takes a uniform row base plus
+    // per-lane constant offsets; other blocks clamp each position into the span.
+    int lane_row[IPW];          // block row this lane moves in instruction i
+    int lane_dst[IPW];          // LDS row base (elements) of instruction i, for K
+    int lane_dstv[IPW];         // ... for V
 #pragma unroll
-        for (int i = 0; i < INSTR_PER_WAVE; ++i) {
-            const int j = wave * INSTR_PER_WAVE + i;     // instruction index
-            const bool is_v = j >= INSTR / 2;            // uniform
-            const int jj = is_v ? j - INSTR / 2 : j;
-            int r0i, r;                                  // first row, this lane's row
-            if constexpr (LPR == 64) {
-                r0i = jj;
-                r = jj;
-            } else {
-                r0i = 16 * (jj >> 3) + (jj & 7);
-                r = r0i + 8 * (lane >> 5);
+    for (int i = 0; i < IPW; ++i) {
+        const int j = wave * IPW + i;
+        const int r0i = (LPR == 64) ? j : 16 * (j >> 3) + (j & 7);
+        lane_row[i] = (LPR == 64) ? j : r0i + 8 * (lane >> 5);
+        lane_dst[i] = row_pos<D, KPADP>(r0i);
+        lane_dstv[i] = row_pos<D, VPADP>(r0i);
+    }
+    const int lane_col = (lane % LPR) * 8;
+    auto dma = [&](const uint16_t* base, uint16_t* stage, const int* dsts, int b) {
+        const int p0 = b * KB;
+        const int s0 = ring ? p0 % cap : p0;
+        if (p0 >= lo_tile && p0 + KB - 1 <= hi_tile && s0 + KB <= cap) {
+            const uint16_t* src = base + (size_t)s0 * D + lane_col;
+#pragma unroll
+            for (int i = 0; i < IPW; ++i)
+                ATTN_DMA16(src + lane_row[i] * D, stage + dsts[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                const int p = min(max(p0 + lane_row[i], lo_tile), hi_tile);
+                const int slot = ring ? p % cap : p;
+                ATTN_DMA16(base + (size_t)slot * D + lane_col, stage + dsts[i]);
             }
-            const int p = min(max(b * KB + r, lo_tile), hi_tile);
-            const int slot = ring ? p % cap : p;
-            const uint16_t* src = (is_v ? Vg : Kg) + (size_t)slot * D + (lane % LPR) * 8;
-            uint16_t* dst = &lds[stage][is_v ? KBLK + row_pos<D, VPADP>(r0i)
-                                             : row_pos<D, KPADP>(r0i)];
-            ATTN_DMA16(src, dst);
         }
     };
 
@@ -147,36 +159,22 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    // per-lane LDS bases: score reads use K row col of tile kt, transpose
-    // reads V rows 32 ks + 4 grp + (col >> 2) (+16); both tile offsets are
-    // compile-time constants (row_pos is linear in whole 16-row groups)
-    const uint16_t* kbase = &lds[0][0] + row_pos<D, KPADP>(col) + 8 * grp;
-    const uint16_t* vbase = &lds[0][0] + KBLK + row_pos<D, VPADP>(4 * grp + (col >> 2)) + 4 * (col & 3);
-    constexpr int K16 = row_pos<D, KPADP>(16);     // offset of the next 16 rows
-    constexpr int V16 = row_pos<D, VPADP>(16);
+    const int kofs = row_pos<D, KPADP>(col) + 8 * grp;
+    const int vofs = row_pos<D, VPADP>(4 * grp + (col >> 2)) + 4 * (col & 3);
 
-    dma_block(b_lo, 0);
-    for (int b = b_lo; b <= b_hi; ++b) {
-        const int stg = (b - b_lo) & 1;
-        __builtin_amdgcn_s_waitcnt(0);           // this wave's part of block b
-        __syncthreads();                          // every wave's part; stage stg^1 free
-        if (b < b_hi) dma_block(b + 1, stg ^ 1);  // in flight while b is multiplied
-        if (!head_ok) continue;
-        const uint16_t* Kl = kbase + stg * (KBLK + VBLK);
-        const uint16_t* Vl = vbase + stg * (KBLK + VBLK);
+    // scores of block b from K stage kl; then the block's softmax: P of the
+    // block in phi / plo, the row sum, and the accumulator rescale
+    u32x4 phi[KS], plo[KS];
+    auto scores_softmax = [&](int b, const uint16_t* kl) {
         const int p0 = b * KB;
-        // every row of the tile sees every key of this block
         const bool interior = p0 >= lo_last && p0 + KB - 1 <= t_first;
-
-        // scores: tile kt holds keys 16 kt + (0..15); lane has keys
-        // 16 kt + 4 grp + i of its row
         float sv[KT][4];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int st = 0; st < QST; ++st)
-                a = mfma_bf16_16x16x32(ld16(Kl + kt * K16 + 32 * st), qreg[st], a);
+                a = mfma_bf16_16x16x32(ld16(kl + kofs + kt * K16 + 32 * st), qreg[st], a);
             if (interior) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sv[kt][i] = a[i] * c;
@@ -201,27 +199,25 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         float psum = 0.f;
         // P.V step ks: lane's k-slots (grp, e) are keys 32 ks + 4 grp + e
         // (e < 4) and 32 ks + 16 + 4 grp + (e - 4), from tiles 2 ks, 2 ks + 1
-        u32x4 phi[KS];
-        u32x4 plo[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int k2 = 0; k2 < KS; ++k2) {
             float pe[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                pe[e] = fast_exp2(sv[2 * ks + (e >> 2)][e & 3] - m_use);
+                pe[e] = fast_exp2(sv[2 * k2 + (e >> 2)][e & 3] - m_use);
                 psum += pe[e];
             }
             uint32_t hw[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) hw[u] = cvt_pk_bf16(pe[2 * u], pe[2 * u + 1]);
-            phi[ks] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+            phi[k2] = u32x4{hw[0], hw[1], hw[2], hw[3]};
             if (PM == ATTN_P_BF16X2) {
                 uint32_t lw[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
                     lw[u] = cvt_pk_bf16(pe[2 * u] - bf16lo_to_f32(hw[u]),
                                         pe[2 * u + 1] - bf16hi_to_f32(hw[u]));
-                plo[ks] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+                plo[k2] = u32x4{lw[0], lw[1], lw[2], lw[3]};
             }
         }
         l_run = l_run * alpha + psum;
@@ -230,19 +226,45 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
         }
-        // V^T operand by transpose reads: lane j of a 16-lane group points at
-        // V row (key of k-slot j >> 2), columns 16 dt + 4 (j & 3) .. +3
+    };
+
+    // O^T += V^T P^T for the block in V stage vl with the P in phi / plo.
+    // V^T operand by transpose reads: lane j of a 16-lane group points at V
+    // row (key of k-slot j >> 2), columns 16 dt + 4 (j & 3) .. +3
+    auto pv = [&](const uint16_t* vl) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int k2 = 0; k2 < KS; ++k2) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const u32x2 x0 = lds_read_tr16(Vl + 2 * ks * V16 + 16 * dt);
-                const u32x2 x1 = lds_read_tr16(Vl + (2 * ks + 1) * V16 + 16 * dt);
+                const u32x2 x0 = lds_read_tr16(vl + vofs + 2 * k2 * V16 + 16 * dt);
+                const u32x2 x1 = lds_read_tr16(vl + vofs + (2 * k2 + 1) * V16 + 16 * dt);
                 const u32x4 a = {x0.x, x0.y, x1.x, x1.y};
-                oacc[dt] = mfma_bf16_16x16x32(a, phi[ks], oacc[dt]);
-                if (PM == ATTN_P_BF16X2) oacc[dt] = mfma_bf16_16x16x32(a, plo[ks], oacc[dt]);
+                oacc[dt] = mfma_bf16_16x16x32(a, phi[k2], oacc[dt]);
+                if (PM == ATTN_P_BF16X2) oacc[dt] = mfma_bf16_16x16x32(a, plo[k2], oacc[dt]);
             }
         }
+    };
+
+    // prologue: K(b_lo), V(b_lo) and K(b_lo + 1) in flight; scores of b_lo
+    dma(Kg, ks_lds[0], lane_dst, b_lo);
+    dma(Vg, vs_lds[0], lane_dstv, b_lo);
+    if (b_lo < b_hi) dma(Kg, ks_lds[1], lane_dst, b_lo + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (head_ok) scores_softmax(b_lo, ks_lds[0]);
+    __syncthreads();                             // K(b_lo) read by every wave
+
+    for (int b = b_lo; b <= b_hi; ++b) {
+        const int st = (b - b_lo) & 1;
+        // in LDS now: V(b) in vs[st], K(b + 1) in ks[st ^ 1]; P(b) in registers
+        if (b + 2 <= b_hi) dma(Kg, ks_lds[st], lane_dst, b + 2);
+        if (b + 1 <= b_hi) dma(Vg, vs_lds[st ^ 1], lane_dstv, b + 1);
+        if (head_ok) {
+            pv(vs_lds[st]);
+            if (b < b_hi) scores_softmax(b + 1, ks_lds[st ^ 1]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);          // this wave's DMAs of K(b+2), V(b+1)
+        __syncthreads();                         // everyone's; K(b+1), V(b) free
     }
 
     const float l_tot = xsum4(l_run);
