@@ -11,23 +11,38 @@ SOURCES = ["api.hip", "decode.hip", "prefill.hip", "cache_write.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Wall", "-Wno-unused-function",
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# per-source extras: the prompt kernel keeps its matrix-core accumulators in
+# ordinary VGPRs (it fits in 256 of them), so rescaling them needs no copies
+# between accumulation and arithmetic registers
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+NOISE = "is not a recognized feature for this target"
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if NOISE not in ln]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + "\n".join(msgs))
+    return msgs
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libgqa_attn.so; returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every HIP source and link libgqa_attn.so; returns its path."""
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs, msgs = [], []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        msgs += _run([HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src),
+                      "-o", obj])
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    msgs += _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     if verbose and msgs:
         print("\n".join(msgs))
     os.replace(tmp, LIB)

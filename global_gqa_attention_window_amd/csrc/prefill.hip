@@ -81,7 +81,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2][VBLK];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lane = tid & 63;
     const int col = lane & 15;
     const int grp = lane >> 4;
@@ -171,10 +171,17 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         float sv[KT][4];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
+            // K operands run PF reads ahead of the products that use them
+            constexpr int PF = 4;
             f32x4 a = {0.f, 0.f, 0.f, 0.f};
+            u32x4 kb[PF];
 #pragma unroll
-            for (int st = 0; st < QST; ++st)
-                a = mfma_bf16_16x16x32(ld16(kl + kofs + kt * K16 + 32 * st), qreg[st], a);
+            for (int st = 0; st < PF; ++st) kb[st] = ld16(kl + kofs + kt * K16 + 32 * st);
+#pragma unroll
+            for (int st = 0; st < QST; ++st) {
+                a = mfma_bf16_16x16x32(kb[st % PF], qreg[st], a);
+                if (st + PF < QST) kb[st % PF] = ld16(kl + kofs + kt * K16 + 32 * (st + PF));
+            }
             if (interior) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sv[kt][i] = a[i] * c;
@@ -234,11 +241,20 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     auto pv = [&](const uint16_t* vl) {
 #pragma unroll
         for (int k2 = 0; k2 < KS; ++k2) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
+            // V^T operands run PF d-tiles ahead of the products that use them
+            constexpr int PF = 4;
+            u32x4 vb[PF];
+            auto rd = [&](int dt) -> u32x4 {
                 const u32x2 x0 = lds_read_tr16(vl + vofs + 2 * k2 * V16 + 16 * dt);
                 const u32x2 x1 = lds_read_tr16(vl + vofs + (2 * k2 + 1) * V16 + 16 * dt);
-                const u32x4 a = {x0.x, x0.y, x1.x, x1.y};
+                return u32x4{x0.x, x0.y, x1.x, x1.y};
+            };
+#pragma unroll
+            for (int dt = 0; dt < PF; ++dt) vb[dt] = rd(dt);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const u32x4 a = vb[dt % PF];
+                if (dt + PF < DT) vb[dt % PF] = rd(dt + PF);
                 oacc[dt] = mfma_bf16_16x16x32(a, phi[k2], oacc[dt]);
                 if (PM == ATTN_P_BF16X2) oacc[dt] = mfma_bf16_16x16x32(a, plo[k2], oacc[dt]);
             }
