@@ -86,9 +86,19 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int col = lane & 15;
     const int grp = lane >> 4;
 
-    const int r0 = blockIdx.x * 16;
-    const int g = blockIdx.y / HG;
-    const int hl = (blockIdx.y % HG) * 4 + wave;
+    // XCD-aware tile order: the hardware deals workgroup L to XCD L % 8, so
+    // L is renumbered to put each XCD on a contiguous range of tiles ordered
+    // KV group, head group, row tile: the workgroups sharing one L2 then
+    // stream the same K/V blocks at about the same time
+    const int n_rt = (n_rows + 15) / 16;
+    const int nwg = n_rt * Hkv * HG;
+    const int L = blockIdx.x;
+    const int lam = (nwg % 8 == 0) ? (L % 8) * (nwg / 8) + L / 8 : L;
+    const int rt = lam % n_rt;
+    const int gh = lam / n_rt;                       // g * HG + head group
+    const int r0 = rt * 16;
+    const int g = gh / HG;
+    const int hl = (gh % HG) * 4 + wave;
     const bool head_ok = hl < G;
     const int h = g * G + (head_ok ? hl : 0);
     const int nvalid = min(16, n_rows - r0);
@@ -308,7 +318,7 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
     const int G = Hq / Hkv;
     const int HG = (G + 3) / 4;
     const float c = scale * ATTN_LOG2E;
-    dim3 grid((n_rows + 15) / 16, Hkv * HG);
+    dim3 grid(((n_rows + 15) / 16) * Hkv * HG);
 #define PREFILL_LAUNCH(DD, PMV)                                                        \
     prefill_kernel<DD, PMV><<<grid, 256, 0, stream>>>(out, q, kc, vc, pos0, n_rows, Hq, \
                                                       Hkv, G, HG, cap, ring, window, c)
