@@ -39,7 +39,23 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=24,
                     help="prompt rows of the oracle's timed sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 4 plain device copies of MIB MiB each (the known-size "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib * 1024 * 1024 // 2
+    src = torch.ones(n, dtype=torch.int16, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 2, "bytes_written": n * 2,
+                      "launches": 4}), flush=True)
 
 
 def causal_pairs(n_rows: int, window: int) -> int:
@@ -95,6 +111,9 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import numpy as np
     import torch
