@@ -68,6 +68,28 @@ ATTN_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 #define ATTN_DMA16(src, lds_base) ((void)(src), (void)(lds_base))
 #endif
 
+// LDS byte address of a __shared__ pointer (the low half of its flat address)
+ATTN_DEV uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)p;
+}
+
+// The same global->LDS load issued from asm.  The compiler then does not see
+// an LDS write, so it adds no wait on the load before later LDS reads (it
+// cannot tell which bytes the load writes and would wait before every read);
+// the caller waits for vmcnt and synchronises before any wave reads the
+// bytes.  lds_byte must be wave-uniform; M0 carries it, with the one wait
+// state an SALU write of M0 needs before an LDS DMA.  Nothing else in a
+// kernel that uses this may rely on M0.
+ATTN_DEV void dma16_asm(const void* src, uint32_t lds_byte) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(lds_byte) : "memory");
+#else
+    (void)src;
+    (void)lds_byte;
+#endif
+}
+
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane j points at four consecutive 16-bit elements M[j][0..3]; lane i gets
 // back M[4 k + (i >> 2)][i & 3] for k = 0..3 (measured on gfx950).  Pointing
@@ -85,17 +107,56 @@ ATTN_DEV u32x2 lds_read_tr16(const uint16_t* p) {
 #endif
 }
 
-// butterfly over the four lanes l, l^16, l^32, l^48 (same l % 16)
+// Butterfly over the four lanes l, l^16, l^32, l^48 (same l % 16), in VALU
+// without an LDS round trip.  v_permlane16_swap_b32 with both operands x
+// hands back (x[l & ~16], x[l | 16]) and v_permlane32_swap_b32 likewise for
+// bit 5, so both lanes of a pair combine the same two values in the same
+// order and end with identical bits.
+ATTN_DEV void pair16(float x, float& a, float& b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+#else
+    a = x; b = x;
+#endif
+}
+ATTN_DEV void pair32(float x, float& a, float& b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+#else
+    a = x; b = x;
+#endif
+}
 ATTN_DEV float xmax4(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    x = fmaxf(x, __shfl_xor(x, 32));
-    return x;
+    float a, b;
+    pair16(x, a, b);
+    x = fmaxf(a, b);
+    pair32(x, a, b);
+    return fmaxf(a, b);
 }
 ATTN_DEV float xsum4(float x) {
-    x += __shfl_xor(x, 16);
-    x += __shfl_xor(x, 32);
-    return x;
+    float a, b;
+    pair16(x, a, b);
+    x = a + b;
+    pair32(x, a, b);
+    return a + b;
 }
+
+// Pinned instruction order inside one scheduling region: each call opens a
+// group of up to n instructions of one kind, groups issue in call order.
+#define ATTN_SG_VALU 0x0002
+#define ATTN_SG_MFMA 0x0008
+#define ATTN_SG_DS_READ 0x0100
+#if defined(__HIP_DEVICE_COMPILE__)
+#define ATTN_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+#else
+#define ATTN_SCHED(mask, n) ((void)0)
+#endif
 
 ATTN_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 ATTN_DEV void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

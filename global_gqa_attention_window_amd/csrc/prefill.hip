@@ -15,19 +15,24 @@
 // heads share every key block: K and V rows land in LDS by direct
 // global->LDS loads (1 KiB of whole rows per instruction, no registers, no
 // VALU), two stages, the next block in flight while the current one is
-// multiplied.  Rows are padded in LDS (K by 16 bytes, V by 32) so that the
-// score reads (eight rows, one 16-byte chunk each) and the transpose reads
-// (four rows, 32 bytes each) fall on distinct banks, and every LDS address
-// is a per-lane base plus a constant offset.  At head dim 256 one DMA
-// instruction moves two 512-byte rows back to back; it takes rows r and
-// r + 8 of a 16-row group, which no read phase uses together, and the
-// padding sits between such pairs.
+// multiplied.  Rows are padded in LDS by 32 bytes so that the score reads
+// (sixteen rows, one 16-byte chunk each) and the transpose reads (four rows,
+// 32 bytes each) fall on distinct banks, and every LDS address is a per-lane
+// base plus a constant offset.  At head dim 256 one DMA instruction moves two
+// 512-byte rows back to back; it takes rows r and r + 8 of a 16-row group,
+// and the padding sits between such pairs.
 //   S^T[key][row] = K . Q^T   v_mfma_f32_16x16x32_bf16: K rows from LDS,
-//                             Q^T resident in registers for the whole walk;
+//                             Q^T resident in AGPRs for the whole walk;
 //   O^T[d][row] += V^T . P^T  v_mfma_f32_16x16x32_bf16 with P (or its bf16
 //                             hi and lo halves, two products) as B; the V^T
 //                             operand comes straight from the row-major V
 //                             block through two transpose reads.
+// One wave runs per SIMD, so the wave itself must keep its matrix unit fed:
+// an iteration issues the scores of block b + 1 (K operands eight products
+// ahead, with the accumulator rescale that block b needs in the VALU slots
+// beside them), then block b's P.V with block b + 1's mask and softmax cut
+// into slices between its products.  Both phases are fenced step by step so
+// the compiler keeps that order.
 // Lane l always owns query row l % 16 (the S^T and O^T column), so the row's
 // maximum, rescale and sum stay in its four lanes (l, l^16, l^32, l^48).
 // Key blocks are KB keys aligned to absolute positions; the running maximum
@@ -55,13 +60,13 @@ ATTN_DEV constexpr int row_pos(int r) {
 }
 
 template <int D, int PM>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                     int pos0, int n_rows, int Hq, int Hkv, int G, int HG, int cap,
                     int ring, int window, float c) {
     constexpr int KB = PrefillCfg<D>::KB;
-    constexpr int KPADP = 8;                 // K padding per row (pair at 256)
+    constexpr int KPADP = 16;                // K padding per row (pair at 256)
     constexpr int VPADP = 16;                // V padding per row (pair at 256)
     constexpr int KBLK = row_pos<D, KPADP>(KB);
     constexpr int VBLK = row_pos<D, VPADP>(KB);
@@ -122,6 +127,10 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         for (int st = 0; st < QST; ++st) {
             u32x4 z = {0u, 0u, 0u, 0u};
             qreg[st] = (row_ok && head_ok) ? ld16(qrow + 32 * st) : z;
+            // Q lives in AGPRs (the products read their B operand from
+            // there), which leaves the VGPRs to the accumulators and to the
+            // operand reads in flight
+            asm volatile("" : "+a"(qreg[st]));
         }
     }
 
@@ -148,17 +157,18 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     auto dma = [&](const uint16_t* base, uint16_t* stage, const int* dsts, int b) {
         const int p0 = b * KB;
         const int s0 = ring ? p0 % cap : p0;
+        const uint32_t lds0 = lds_addr(stage);
         if (p0 >= lo_tile && p0 + KB - 1 <= hi_tile && s0 + KB <= cap) {
             const uint16_t* src = base + (size_t)s0 * D + lane_col;
 #pragma unroll
             for (int i = 0; i < IPW; ++i)
-                ATTN_DMA16(src + lane_row[i] * D, stage + dsts[i]);
+                dma16_asm(src + lane_row[i] * D, lds0 + 2 * dsts[i]);
         } else {
 #pragma unroll
             for (int i = 0; i < IPW; ++i) {
                 const int p = min(max(p0 + lane_row[i], lo_tile), hi_tile);
                 const int slot = ring ? p % cap : p;
-                ATTN_DMA16(base + (size_t)slot * D + lane_col, stage + dsts[i]);
+                dma16_asm(base + (size_t)slot * D + lane_col, lds0 + 2 * dsts[i]);
             }
         }
     };
@@ -172,125 +182,207 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int kofs = row_pos<D, KPADP>(col) + 8 * grp;
     const int vofs = row_pos<D, VPADP>(4 * grp + (col >> 2)) + 4 * (col & 3);
 
-    // scores of block b from K stage kl; then the block's softmax: P of the
-    // block in phi / plo, the row sum, and the accumulator rescale
-    u32x4 phi[KS], plo[KS];
-    auto scores_softmax = [&](int b, const uint16_t* kl) {
-        const int p0 = b * KB;
-        const bool interior = p0 >= lo_last && p0 + KB - 1 <= t_first;
-        float sv[KT][4];
+    constexpr int NS = KT * QST;                 // score products per block
+    constexpr int KPF = 8;                       // K operand reads in flight
+    constexpr int NPV = KS * DT;                 // V^T operands per block
+    constexpr int VPF = 4;                       // V^T operands in flight
+    constexpr int NE = 8 * KS;                   // probabilities per lane per block
+    static_assert(KPF == 2 * VPF, "the V^T reads fill the last KPF score steps");
+
+    // K operand of score product j: tile j % KT, reduction step j / KT
+    auto rd_k = [&](const uint16_t* kl, int j) {
+        return ld16(kl + kofs + (j % KT) * K16 + 32 * (j / KT));
+    };
+    // V^T operand i (P.V step i / DT, d tile i % DT) by two transpose reads:
+    // lane j of a 16-lane group points at V row (key of k-slot j >> 2),
+    // columns 16 dt + 4 (j & 3) .. +3
+    auto rd_v = [&](const uint16_t* vl, int i) -> u32x4 {
+        const int k2 = i / DT, dt = i % DT;
+        const u32x2 x0 = lds_read_tr16(vl + vofs + 2 * k2 * V16 + 16 * dt);
+        const u32x2 x1 = lds_read_tr16(vl + vofs + (2 * k2 + 1) * V16 + 16 * dt);
+        return u32x4{x0.x, x0.y, x1.x, x1.y};
+    };
+
+    // Score phase of a block: S^T from K stage kl into sacc (lane: keys
+    // 16 kt + 4 grp + i of tile kt, query row col), the accumulator taken to
+    // the running maximum of the previous block (factor alpha; exactly 1
+    // keeps the bits), and the first VPF V^T operands of the P.V that
+    // follows, from V stage vl.  Step j issues product j, the LDS read KPF
+    // products ahead (K operands, then the V^T halves) and its share of the
+    // rescale, fenced so that the products never wait on LDS and the
+    // multiplies fill the VALU slots beside them.
+    constexpr int RPS = 4 * DT / NS;             // rescale multiplies per step
+    static_assert(RPS * NS == 4 * DT, "rescale split");
+    auto score_phase = [&](const uint16_t* kl, const uint16_t* vl, f32x4 (&sacc)[KT],
+                           u32x4 (&vb)[VPF], float alpha) {
+        u32x4 kb[KPF];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-            // K operands run PF reads ahead of the products that use them
-            constexpr int PF = 4;
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            u32x4 kb[PF];
+        for (int j = 0; j < KPF; ++j) kb[j] = rd_k(kl, j);
 #pragma unroll
-            for (int st = 0; st < PF; ++st) kb[st] = ld16(kl + kofs + kt * K16 + 32 * st);
+        for (int kt = 0; kt < KT; ++kt) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        u32x2 vhalf = {0u, 0u};
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int st = 0; st < QST; ++st) {
-                a = mfma_bf16_16x16x32(kb[st % PF], qreg[st], a);
-                if (st + PF < QST) kb[st % PF] = ld16(kl + kofs + kt * K16 + 32 * (st + PF));
-            }
-            if (interior) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sv[kt][i] = a[i] * c;
+        for (int j = 0; j < NS; ++j) {
+            sacc[j % KT] = mfma_bf16_16x16x32(kb[j % KPF], qreg[j / KT], sacc[j % KT]);
+            const int r = j + KPF;               // the read issued at this step
+            if (r < NS) {
+                kb[j % KPF] = rd_k(kl, r);
             } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int p = p0 + 16 * kt + 4 * grp + i;
-                    const bool ok = row_ok && p <= t_row && p >= lo_row;
-                    sv[kt][i] = ok ? a[i] * c : -INFINITY;
-                }
+                const int h = r - NS;            // V^T operand h / 2, half h & 1
+                const int i = h >> 1, k2 = i / DT, dt = i % DT;
+                const u32x2 x = lds_read_tr16(vl + vofs + (2 * k2 + (h & 1)) * V16 + 16 * dt);
+                if ((h & 1) == 0) vhalf = x;
+                else vb[i] = u32x4{vhalf.x, vhalf.y, x.x, x.y};
             }
-        }
-        float mx = sv[0][0];
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sv[kt][i]);
-        mx = xmax4(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
-        float psum = 0.f;
-        // P.V step ks: lane's k-slots (grp, e) are keys 32 ks + 4 grp + e
-        // (e < 4) and 32 ks + 16 + 4 grp + (e - 4), from tiles 2 ks, 2 ks + 1
-#pragma unroll
-        for (int k2 = 0; k2 < KS; ++k2) {
-            float pe[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                pe[e] = fast_exp2(sv[2 * k2 + (e >> 2)][e & 3] - m_use);
-                psum += pe[e];
+            for (int u = 0; u < RPS; ++u) {
+                const int e = j * RPS + u;       // accumulator element e
+                oacc[e / 4][e % 4] *= alpha;
             }
-            uint32_t hw[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) hw[u] = cvt_pk_bf16(pe[2 * u], pe[2 * u + 1]);
-            phi[k2] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-            if (PM == ATTN_P_BF16X2) {
-                uint32_t lw[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    lw[u] = cvt_pk_bf16(pe[2 * u] - bf16lo_to_f32(hw[u]),
-                                        pe[2 * u + 1] - bf16hi_to_f32(hw[u]));
-                plo[k2] = u32x4{lw[0], lw[1], lw[2], lw[3]};
-            }
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // O^T += V^T P^T for the block in V stage vl with the P in phi / plo.
-    // V^T operand by transpose reads: lane j of a 16-lane group points at V
-    // row (key of k-slot j >> 2), columns 16 dt + 4 (j & 3) .. +3
-    auto pv = [&](const uint16_t* vl) {
+    // Softmax of block b from its raw scores, in slices that the P.V of the
+    // previous block interleaves: the causal / window mask, P in qh (and the
+    // low halves in ql), the row sum folded into l_run, and the factor that
+    // takes the accumulator to the new running maximum.  A key p of the
+    // block is attended when lo_row <= p <= t_row, one unsigned compare of
+    // p - lo_row against t_row - lo_row; rows past the chunk end score finite
+    // values against finite keys and are never stored.  The scale c > 0 is
+    // applied inside the exponent: the row maximum of c s is c times that of
+    // s (rounding is monotone), and exp2(c s - m) takes one fused rounding.
+    // Probability e sits in tile e >> 2, element e & 3: P.V step e >> 3,
+    // k-slot (grp, e & 7), i.e. keys 32 ks + 4 grp + (e & 3) + 16 ((e >> 2) & 1).
+    constexpr int SL_MAX = KT;                   // slices 0 .. KT-1 mask a tile each
+    constexpr int SL_EXP = KT + 4;
+    constexpr int SL_CVT = SL_EXP + NE;
+    constexpr int NSLICE = SL_CVT + NE / 2;      // the row sum rides on the last one
+    const uint32_t span = (uint32_t)(t_row - lo_row);
+    float sm_mx = 0.f, sm_mnew = 0.f, sm_muse = 0.f, sm_alpha = 1.f, sm_psum = 0.f;
+    float sm_pe[NE];
+    auto softmax_slice = [&](int sl, int b, f32x4 (&sacc)[KT], u32x4 (&qh)[KS],
+                             u32x4 (&ql)[KS]) {
+        if (sl < SL_MAX) {
+            const int kt = sl;
+            const int d0 = b * KB + 16 * kt + 4 * grp - lo_row;
 #pragma unroll
-        for (int k2 = 0; k2 < KS; ++k2) {
-            // V^T operands run PF d-tiles ahead of the products that use them
-            constexpr int PF = 4;
-            u32x4 vb[PF];
-            auto rd = [&](int dt) -> u32x4 {
-                const u32x2 x0 = lds_read_tr16(vl + vofs + 2 * k2 * V16 + 16 * dt);
-                const u32x2 x1 = lds_read_tr16(vl + vofs + (2 * k2 + 1) * V16 + 16 * dt);
-                return u32x4{x0.x, x0.y, x1.x, x1.y};
-            };
+            for (int i = 0; i < 4; ++i)
+                sacc[kt][i] = ((uint32_t)(d0 + i) <= span) ? sacc[kt][i] : -INFINITY;
+        } else if (sl == SL_MAX) {
+            float mx = sacc[0][0];
 #pragma unroll
-            for (int dt = 0; dt < PF; ++dt) vb[dt] = rd(dt);
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const u32x4 a = vb[dt % PF];
-                if (dt + PF < DT) vb[dt % PF] = rd(dt + PF);
-                oacc[dt] = mfma_bf16_16x16x32(a, phi[k2], oacc[dt]);
-                if (PM == ATTN_P_BF16X2) oacc[dt] = mfma_bf16_16x16x32(a, plo[k2], oacc[dt]);
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kt][i]);
+            sm_mx = mx;
+        } else if (sl == SL_MAX + 1) {
+            float a, b2;
+            pair16(sm_mx, a, b2);
+            sm_mx = fmaxf(a, b2);
+        } else if (sl == SL_MAX + 2) {
+            float a, b2;
+            pair32(sm_mx, a, b2);
+            sm_mnew = fmaxf(m_run, fmaxf(a, b2) * c);
+            sm_muse = (sm_mnew == -INFINITY) ? 0.f : sm_mnew;
+            sm_psum = 0.f;
+        } else if (sl == SL_MAX + 3) {
+            sm_alpha = fast_exp2(m_run - sm_muse);
+        } else if (sl < SL_CVT) {
+            const int e = sl - SL_EXP;
+            sm_pe[e] = fast_exp2(fmaf(sacc[e >> 2][e & 3], c, -sm_muse));
+            sm_psum += sm_pe[e];
+        } else if (sl < NSLICE) {
+            const int u = sl - SL_CVT;
+            const uint32_t hw = cvt_pk_bf16(sm_pe[2 * u], sm_pe[2 * u + 1]);
+            qh[u / 4][u % 4] = hw;
+            if (PM == ATTN_P_BF16X2)
+                ql[u / 4][u % 4] = cvt_pk_bf16(sm_pe[2 * u] - bf16lo_to_f32(hw),
+                                               sm_pe[2 * u + 1] - bf16hi_to_f32(hw));
+            if (sl == NSLICE - 1) {
+                l_run = l_run * sm_alpha + sm_psum;
+                m_run = sm_mnew;
             }
         }
     };
+    static_assert(NSLICE <= NPV, "the softmax fits beside one P.V");
 
-    // prologue: K(b_lo), V(b_lo) and K(b_lo + 1) in flight; scores of b_lo
+    // P.V of a block (V stage vl, first VPF operands already in vb, P in
+    // ph / pl) with the next block's softmax beside it: step i issues the
+    // products of operand i, the read of operand i + VPF and one softmax
+    // slice, fenced so that the order holds.
+    auto pv_phase = [&](const uint16_t* vl, u32x4 (&vb)[VPF], const u32x4 (&ph)[KS],
+                        const u32x4 (&pl)[KS], int bn, f32x4 (&sacc)[KT], u32x4 (&qh)[KS],
+                        u32x4 (&ql)[KS]) {
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const int k2 = i / DT, dt = i % DT;
+            const u32x4 a = vb[i % VPF];
+            if (i + VPF < NPV) vb[i % VPF] = rd_v(vl, i + VPF);
+            oacc[dt] = mfma_bf16_16x16x32(a, ph[k2], oacc[dt]);
+            if (PM == ATTN_P_BF16X2) oacc[dt] = mfma_bf16_16x16x32(a, pl[k2], oacc[dt]);
+            softmax_slice(i, bn, sacc, qh, ql);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // P of the block whose P.V comes next, and the next block's
+    u32x4 pch[KS], pcl[KS], pnh[KS], pnl[KS];
+#pragma unroll
+    for (int k2 = 0; k2 < KS; ++k2) {
+        pch[k2] = u32x4{0u, 0u, 0u, 0u};
+        pcl[k2] = u32x4{0u, 0u, 0u, 0u};
+        pnh[k2] = u32x4{0u, 0u, 0u, 0u};
+        pnl[k2] = u32x4{0u, 0u, 0u, 0u};
+    }
+    u32x4 vb[VPF];
+
+    // prologue: K(b_lo), V(b_lo) and K(b_lo + 1) in flight; softmax of b_lo
     dma(Kg, ks_lds[0], lane_dst, b_lo);
     dma(Vg, vs_lds[0], lane_dstv, b_lo);
     if (b_lo < b_hi) dma(Kg, ks_lds[1], lane_dst, b_lo + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (head_ok) scores_softmax(b_lo, ks_lds[0]);
+    if (head_ok) {
+        f32x4 sacc[KT];
+        score_phase(ks_lds[0], vs_lds[0], sacc, vb, 1.f);
+#pragma unroll
+        for (int sl = 0; sl < NSLICE; ++sl) softmax_slice(sl, b_lo, sacc, pch, pcl);
+    }
     __syncthreads();                             // K(b_lo) read by every wave
 
-    for (int b = b_lo; b <= b_hi; ++b) {
+    // Iteration b: the scores of block b + 1 (with the rescale that block b
+    // needs), then block b's P.V beside block b + 1's softmax.
+    for (int b = b_lo; b < b_hi; ++b) {
         const int st = (b - b_lo) & 1;
-        // in LDS now: V(b) in vs[st], K(b + 1) in ks[st ^ 1]; P(b) in registers
+        // in LDS now: V(b) in vs[st], K(b + 1) in ks[st ^ 1]; P(b) in pch / pcl
         if (b + 2 <= b_hi) dma(Kg, ks_lds[st], lane_dst, b + 2);
-        if (b + 1 <= b_hi) dma(Vg, vs_lds[st ^ 1], lane_dstv, b + 1);
+        dma(Vg, vs_lds[st ^ 1], lane_dstv, b + 1);
         if (head_ok) {
-            pv(vs_lds[st]);
-            if (b < b_hi) scores_softmax(b + 1, ks_lds[st ^ 1]);
+            f32x4 sacc[KT];
+            score_phase(ks_lds[st ^ 1], vs_lds[st], sacc, vb, sm_alpha);
+            pv_phase(vs_lds[st], vb, pch, pcl, b + 1, sacc, pnh, pnl);
+#pragma unroll
+            for (int k2 = 0; k2 < KS; ++k2) {
+                pch[k2] = pnh[k2];
+                pcl[k2] = pnl[k2];
+            }
         }
         __builtin_amdgcn_s_waitcnt(0);          // this wave's DMAs of K(b+2), V(b+1)
         __syncthreads();                         // everyone's; K(b+1), V(b) free
+    }
+    if (head_ok) {
+        const uint16_t* vl = vs_lds[(b_hi - b_lo) & 1];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= sm_alpha;
+#pragma unroll
+        for (int i = 0; i < NPV; ++i) {
+            const int k2 = i / DT, dt = i % DT;
+            const u32x4 a = rd_v(vl, i);
+            oacc[dt] = mfma_bf16_16x16x32(a, pch[k2], oacc[dt]);
+            if (PM == ATTN_P_BF16X2) oacc[dt] = mfma_bf16_16x16x32(a, pcl[k2], oacc[dt]);
+        }
     }
 
     const float l_tot = xsum4(l_run);
