@@ -89,6 +89,23 @@ ATTN_DEV void dma16_asm(const void* src, uint32_t lds_byte) {
     (void)lds_byte;
 #endif
 }
+// ... with a wave-uniform base address and a per-lane 32-bit byte offset
+// (both wave-uniform by construction; readfirstlane puts them in SGPRs where
+// the compiler cannot prove it)
+ATTN_DEV void dma16_asm_sbase(const void* base, uint32_t voff, uint32_t lds_byte) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint64_t b64 = (uint64_t)(uintptr_t)base;
+    const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+    const uint32_t lu = __builtin_amdgcn_readfirstlane(lds_byte);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(voff), "s"(bu), "s"(lu) : "memory");
+#else
+    (void)base;
+    (void)voff;
+    (void)lds_byte;
+#endif
+}
 
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane j points at four consecutive 16-bit elements M[j][0..3]; lane i gets

@@ -59,6 +59,35 @@ ATTN_DEV constexpr int row_pos(int r) {
     }
 }
 
+// Operations per stage of the staged softmax (see the kernel) for NE
+// probabilities per lane, and the P.V steps its plan takes at cap
+// operations per step.
+template <int NE, bool X2>
+__host__ __device__ constexpr int sm_stage_ops(int k) {
+    constexpr int NP = NE / 2;
+    constexpr int NMX = (NE + 2) / 3;
+    constexpr int NMX2 = (NMX + 2) / 3;
+    switch (k) {
+        case 0: return NMX;
+        case 1: return NMX2;
+        case 2: return NMX2 > 1 ? 1 : 0;
+        case 3: case 4: case 5: case 6: case 7: return 1;
+        case 8: return 2;
+        case 9: case 10: return 1 + NE;
+        case 11: return NE / 2 + NP;
+        case 12: return NE / 4 + (X2 ? 2 * NP : 0);
+        case 13: return NE / 8 + (X2 ? 2 * NP : 0);
+        case 14: return NE / 16 + (X2 ? NP : 0);
+        default: return 1;
+    }
+}
+template <int NE, bool X2>
+__host__ __device__ constexpr int sm_plan_steps(int cap, int nstg) {
+    int t = 0;
+    for (int k = 0; k < nstg; ++k) t += (sm_stage_ops<NE, X2>(k) + cap - 1) / cap;
+    return t;
+}
+
 template <int D, int PM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
@@ -84,6 +113,8 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     // two K stages and two V stages: K runs one block ahead of V
     __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][KBLK];
     __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2][VBLK];
+    // landing row of the L2 prefetch loads (written, never read)
+    __shared__ __attribute__((aligned(16))) uint16_t pf_lds[2][512];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -139,38 +170,80 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 
     // DMA of one K or V block: instruction j (wave w issues [w IPW, (w+1) IPW))
     // moves 1 KiB: block row j at D=512, rows 16 (j >> 3) + (j & 7) and +8 at
-    // D=256 (lanes 0..31 and 32..63).  A block whose KB positions all lie in
-    // the tile's span and do not wrap the ring takes a uniform row base plus
-    // per-lane constant offsets; other blocks clamp each position into the span.
+    // D=256 (lanes 0..31 and 32..63).  dma_plan picks the sources of the
+    // wave's IPW instructions (a wave-uniform base and per-lane 32-bit byte
+    // offsets), dma_issue sends one, so the loop can spread them between its
+    // products.  A block whose KB positions all lie in the tile's span and do
+    // not wrap the ring takes the base of its first slot and per-lane constant
+    // offsets; other blocks clamp each position into the span (a block past
+    // the tile's last one reads its last key).
+    // The workgroups of one XCD stream the same blocks at about the same
+    // time; each starts its instructions at a different row (rotation by its
+    // index on the XCD) so that their requests spread over the L2 channels
+    // instead of queueing on the few that hold the same lines.
     int lane_row[IPW];          // block row this lane moves in instruction i
     int lane_dst[IPW];          // LDS row base (elements) of instruction i, for K
     int lane_dstv[IPW];         // ... for V
+    const int rot = __builtin_amdgcn_readfirstlane((int)((blockIdx.x >> 3) * 7u) % INSTR);
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
-        const int j = wave * IPW + i;
+        const int j = (wave * IPW + i + rot) % INSTR;
         const int r0i = (LPR == 64) ? j : 16 * (j >> 3) + (j & 7);
         lane_row[i] = (LPR == 64) ? j : r0i + 8 * (lane >> 5);
         lane_dst[i] = row_pos<D, KPADP>(r0i);
         lane_dstv[i] = row_pos<D, VPADP>(r0i);
     }
     const int lane_col = (lane % LPR) * 8;
-    auto dma = [&](const uint16_t* base, uint16_t* stage, const int* dsts, int b) {
+    uint32_t lane_off[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) lane_off[i] = (uint32_t)(lane_row[i] * D + lane_col) * 2u;
+    auto dma_plan = [&](const uint16_t* g, uint16_t* stage, int b, const uint16_t*& base,
+                        uint32_t (&voff)[IPW], uint32_t& lds0) {
         const int p0 = b * KB;
         const int s0 = ring ? p0 % cap : p0;
-        const uint32_t lds0 = lds_addr(stage);
+        lds0 = lds_addr(stage);
         if (p0 >= lo_tile && p0 + KB - 1 <= hi_tile && s0 + KB <= cap) {
-            const uint16_t* src = base + (size_t)s0 * D + lane_col;
+            base = g + (size_t)s0 * D;
 #pragma unroll
-            for (int i = 0; i < IPW; ++i)
-                dma16_asm(src + lane_row[i] * D, lds0 + 2 * dsts[i]);
+            for (int i = 0; i < IPW; ++i) voff[i] = lane_off[i];
         } else {
+            base = g;
 #pragma unroll
             for (int i = 0; i < IPW; ++i) {
                 const int p = min(max(p0 + lane_row[i], lo_tile), hi_tile);
                 const int slot = ring ? p % cap : p;
-                dma16_asm(base + (size_t)slot * D + lane_col, lds0 + 2 * dsts[i]);
+                voff[i] = (uint32_t)(slot * D + lane_col) * 2u;
             }
         }
+    };
+    auto dma_issue = [&](const uint16_t* base, const uint32_t (&voff)[IPW], uint32_t lds0,
+                         const int* dsts, int i) {
+        dma16_asm_sbase(base, voff[i], lds0 + 2u * (uint32_t)dsts[i]);
+    };
+    auto dma = [&](const uint16_t* g, uint16_t* stage, const int* dsts, int b) {
+        const uint16_t* base;
+        uint32_t voff[IPW], lds0;
+        dma_plan(g, stage, b, base, voff, lds0);
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) dma_issue(base, voff, lds0, dsts, i);
+    };
+    constexpr int DMA_EVERY = 4;                 // fenced steps between DMA issues
+
+    // L2 prefetch.  Each XCD fetches every K/V block from memory once, and
+    // its workgroups, which walk the blocks in step, would all wait on that
+    // miss; so the workgroups of an XCD share out block b + PF_AHEAD one
+    // 1 KiB slice each (row tile rt: K slice in wave 0, V slice in wave 1)
+    // and load it early into a scratch row, making the block's DMAs L2 hits.
+    constexpr int PF_AHEAD = 4;
+    constexpr int PF_ROWS = 512 / D;             // block rows per 1 KiB slice
+    auto l2_prefetch = [&](int b) {
+        if (wave >= 2) return;
+        const int r = (rt * PF_ROWS) % KB + (lane * 8) / D;
+        const int p = min(b * KB + r, hi_tile);
+        const int slot = ring ? p % cap : p;
+        const uint16_t* g = wave == 0 ? Kg : Vg;
+        dma16_asm_sbase(g, (uint32_t)(slot * D + (lane * 8) % D) * 2u,
+                        lds_addr(pf_lds[wave]));
     };
 
     f32x4 oacc[DT];
@@ -182,12 +255,30 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int kofs = row_pos<D, KPADP>(col) + 8 * grp;
     const int vofs = row_pos<D, VPADP>(4 * grp + (col >> 2)) + 4 * (col & 3);
 
+    // a block needs no per-key mask when every row of the tile attends all
+    // of its keys; the others mask keys outside [lo_row, t_row] with -inf
+    auto is_interior = [&](int b) {
+        const int p0 = b * KB;
+        return p0 >= lo_last && p0 + KB - 1 <= t_first;
+    };
+    auto mask = [&](int b, f32x4 (&sacc)[KT]) {
+        const int p0 = b * KB;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int p = p0 + 16 * kt + 4 * grp + i;
+                sacc[kt][i] = (p >= lo_row && p <= t_row) ? sacc[kt][i] : -INFINITY;
+            }
+    };
+
     constexpr int NS = KT * QST;                 // score products per block
     constexpr int KPF = 8;                       // K operand reads in flight
     constexpr int NPV = KS * DT;                 // V^T operands per block
     constexpr int VPF = 4;                       // V^T operands in flight
     constexpr int NE = 8 * KS;                   // probabilities per lane per block
     static_assert(KPF == 2 * VPF, "the V^T reads fill the last KPF score steps");
+    static_assert(IPW * DMA_EVERY <= NS && IPW * DMA_EVERY <= NPV, "DMA issues fit the steps");
 
     // K operand of score product j: tile j % KT, reduction step j / KT
     auto rd_k = [&](const uint16_t* kl, int j) {
@@ -214,7 +305,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     constexpr int RPS = 4 * DT / NS;             // rescale multiplies per step
     static_assert(RPS * NS == 4 * DT, "rescale split");
     auto score_phase = [&](const uint16_t* kl, const uint16_t* vl, f32x4 (&sacc)[KT],
-                           u32x4 (&vb)[VPF], float alpha) {
+                           u32x4 (&vb)[VPF], float alpha, auto&& hook) {
         u32x4 kb[KPF];
 #pragma unroll
         for (int j = 0; j < KPF; ++j) kb[j] = rd_k(kl, j);
@@ -240,81 +331,132 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                 const int e = j * RPS + u;       // accumulator element e
                 oacc[e / 4][e % 4] *= alpha;
             }
+            hook(j);
             __builtin_amdgcn_sched_barrier(0);
         }
+        // the rescaled accumulator is used here, so the multiplies stay in
+        // this phase rather than sinking past the mask branch
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) asm volatile("" :: "v"(oacc[dt]));
     };
 
-    // Softmax of block b from its raw scores, in slices that the P.V of the
-    // previous block interleaves: the causal / window mask, P in qh (and the
-    // low halves in ql), the row sum folded into l_run, and the factor that
-    // takes the accumulator to the new running maximum.  A key p of the
-    // block is attended when lo_row <= p <= t_row, one unsigned compare of
-    // p - lo_row against t_row - lo_row; rows past the chunk end score finite
-    // values against finite keys and are never stored.  The scale c > 0 is
-    // applied inside the exponent: the row maximum of c s is c times that of
-    // s (rounding is monotone), and exp2(c s - m) takes one fused rounding.
-    // Probability e sits in tile e >> 2, element e & 3: P.V step e >> 3,
-    // k-slot (grp, e & 7), i.e. keys 32 ks + 4 grp + (e & 3) + 16 ((e >> 2) & 1).
-    constexpr int SL_MAX = KT;                   // slices 0 .. KT-1 mask a tile each
-    constexpr int SL_EXP = KT + 4;
-    constexpr int SL_CVT = SL_EXP + NE;
-    constexpr int NSLICE = SL_CVT + NE / 2;      // the row sum rides on the last one
-    const uint32_t span = (uint32_t)(t_row - lo_row);
-    float sm_mx = 0.f, sm_mnew = 0.f, sm_muse = 0.f, sm_alpha = 1.f, sm_psum = 0.f;
-    float sm_pe[NE];
-    auto softmax_slice = [&](int sl, int b, f32x4 (&sacc)[KT], u32x4 (&qh)[KS],
-                             u32x4 (&ql)[KS]) {
-        if (sl < SL_MAX) {
-            const int kt = sl;
-            const int d0 = b * KB + 16 * kt + 4 * grp - lo_row;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sacc[kt][i] = ((uint32_t)(d0 + i) <= span) ? sacc[kt][i] : -INFINITY;
-        } else if (sl == SL_MAX) {
-            float mx = sacc[0][0];
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kt][i]);
-            sm_mx = mx;
-        } else if (sl == SL_MAX + 1) {
-            float a, b2;
-            pair16(sm_mx, a, b2);
-            sm_mx = fmaxf(a, b2);
-        } else if (sl == SL_MAX + 2) {
-            float a, b2;
-            pair32(sm_mx, a, b2);
-            sm_mnew = fmaxf(m_run, fmaxf(a, b2) * c);
-            sm_muse = (sm_mnew == -INFINITY) ? 0.f : sm_mnew;
-            sm_psum = 0.f;
-        } else if (sl == SL_MAX + 3) {
-            sm_alpha = fast_exp2(m_run - sm_muse);
-        } else if (sl < SL_CVT) {
-            const int e = sl - SL_EXP;
-            sm_pe[e] = fast_exp2(fmaf(sacc[e >> 2][e & 3], c, -sm_muse));
-            sm_psum += sm_pe[e];
-        } else if (sl < NSLICE) {
-            const int u = sl - SL_CVT;
-            const uint32_t hw = cvt_pk_bf16(sm_pe[2 * u], sm_pe[2 * u + 1]);
-            qh[u / 4][u % 4] = hw;
-            if (PM == ATTN_P_BF16X2)
-                ql[u / 4][u % 4] = cvt_pk_bf16(sm_pe[2 * u] - bf16lo_to_f32(hw),
-                                               sm_pe[2 * u + 1] - bf16hi_to_f32(hw));
-            if (sl == NSLICE - 1) {
-                l_run = l_run * sm_alpha + sm_psum;
-                m_run = sm_mnew;
+    // Softmax of a block from its masked raw scores, cut into stages for
+    // the P.V of the previous block to carry: P in qh (and the low halves in
+    // ql), the row sum folded into l_run, and the factor sm_alpha that takes
+    // the accumulator to the new running maximum.  The operations of a stage
+    // are independent of one another and use only results of earlier
+    // stages, and a stage spreads over ceil(ops / SM_CAP) P.V steps, so no
+    // VALU instruction waits on its neighbour while products are due.  The
+    // scale c > 0 is applied inside the exponent: the row maximum of c s is c
+    // times that of s (rounding is monotone), and exp2(c s - m) takes one
+    // fused rounding; m is clamped to -FLT_MAX so a fully masked row gives
+    // exp2(-inf) = 0.  The row sum adds pairwise.  Probability e sits in
+    // tile e >> 2, element e & 3: P.V step e >> 3, k-slot (grp, e & 7), i.e.
+    // keys 32 ks + 4 grp + (e & 3) + 16 ((e >> 2) & 1).
+    constexpr bool X2 = PM == ATTN_P_BF16X2;
+    constexpr int NP = NE / 2;                   // packed pairs of P
+    constexpr int NMX = (NE + 2) / 3;            // first-level max3 partials
+    constexpr int NMX2 = (NMX + 2) / 3;
+    constexpr int SM_CAP = X2 ? 6 : (NE > 8 ? 4 : 3);   // VALU ops per P.V step
+    constexpr int NSTG = 16;
+    constexpr int SM_STEPS = sm_plan_steps<NE, X2>(SM_CAP, NSTG);
+    static_assert(NMX2 <= 2, "two second-level partial maxima at most");
+    float sm_pm[NMX], sm_pm2[NMX2], sm_mx = 0.f, sm_mnew = 0.f, sm_muse = 0.f;
+    float sm_aarg = 0.f, sm_alpha = 1.f;
+    float sm_t[NE], sm_pe[NE], sm_ps1[NE / 2], sm_ps2[NE / 4], sm_ps3[(NE + 7) / 8];
+    float sm_ps4 = 0.f, sm_a = 0.f, sm_b = 0.f;
+    float sm_r[2 * NP];
+    uint32_t sm_hw[NP];
+    auto sm_op = [&](int k, int o, f32x4 (&sacc)[KT], u32x4 (&qh)[KS], u32x4 (&ql)[KS]) {
+        auto sv = [&](int e) { return sacc[e >> 2][e & 3]; };
+        if (k == 0) {                                  // partial maxima
+            const int e = 3 * o;
+            sm_pm[o] = (e + 2 < NE) ? fmaxf(fmaxf(sv(e), sv(e + 1)), sv(e + 2))
+                     : (e + 1 < NE) ? fmaxf(sv(e), sv(e + 1)) : sv(e);
+        } else if (k == 1) {
+            const int e = 3 * o;
+            sm_pm2[o] = (e + 2 < NMX) ? fmaxf(fmaxf(sm_pm[e], sm_pm[e + 1]), sm_pm[e + 2])
+                      : (e + 1 < NMX) ? fmaxf(sm_pm[e], sm_pm[e + 1]) : sm_pm[e];
+            if (NMX2 == 1) sm_mx = sm_pm2[0];
+        } else if (k == 2) {
+            sm_mx = (NMX2 > 1) ? fmaxf(sm_pm2[0], sm_pm2[NMX2 - 1]) : sm_pm2[0];
+        } else if (k == 3) {
+            pair16(sm_mx, sm_a, sm_b);
+        } else if (k == 4) {
+            sm_mx = fmaxf(sm_a, sm_b);
+        } else if (k == 5) {
+            pair32(sm_mx, sm_a, sm_b);
+        } else if (k == 6) {
+            sm_mx = fmaxf(sm_a, sm_b);
+        } else if (k == 7) {
+            sm_mx *= c;
+        } else if (k == 8) {
+            if (o == 0) sm_mnew = fmaxf(m_run, sm_mx);
+            else sm_muse = fmaxf(fmaxf(m_run, sm_mx), -__FLT_MAX__);
+        } else if (k == 9) {
+            if (o == 0) sm_aarg = m_run - sm_muse;
+            else sm_t[o - 1] = fmaf(sv(o - 1), c, -sm_muse);
+        } else if (k == 10) {
+            if (o == 0) sm_alpha = fast_exp2(sm_aarg);
+            else sm_pe[o - 1] = fast_exp2(sm_t[o - 1]);
+        } else if (k == 11) {
+            if (o < NE / 2) {
+                sm_ps1[o] = sm_pe[2 * o] + sm_pe[2 * o + 1];
+            } else {
+                const int u = o - NE / 2;
+                sm_hw[u] = cvt_pk_bf16(sm_pe[2 * u], sm_pe[2 * u + 1]);
+                qh[u / 4][u % 4] = sm_hw[u];
             }
+        } else if (k == 12) {
+            if (o < NE / 4) {
+                sm_ps2[o] = sm_ps1[2 * o] + sm_ps1[2 * o + 1];
+            } else {
+                const int v = o - NE / 4;                  // hi halves back to fp32
+                sm_r[v] = (v & 1) ? bf16hi_to_f32(sm_hw[v >> 1]) : bf16lo_to_f32(sm_hw[v >> 1]);
+            }
+        } else if (k == 13) {
+            if (o < NE / 8) {
+                sm_ps3[o] = sm_ps2[2 * o] + sm_ps2[2 * o + 1];
+            } else {
+                const int v = o - NE / 8;                  // residuals
+                sm_r[v] = sm_pe[v] - sm_r[v];
+            }
+        } else if (k == 14) {
+            if (o < NE / 16) {
+                sm_ps4 = sm_ps3[0] + sm_ps3[(NE >= 16) ? 1 : 0];
+            } else {
+                const int u = o - NE / 16;
+                ql[u / 4][u % 4] = cvt_pk_bf16(sm_r[2 * u], sm_r[2 * u + 1]);
+            }
+        } else if (k == 15) {
+            const float psum = (NE >= 16) ? sm_ps4 : (NE >= 8) ? sm_ps3[0] : sm_ps2[0];
+            l_run = fmaf(l_run, sm_alpha, psum);
+            m_run = sm_mnew;
         }
     };
-    static_assert(NSLICE <= NPV, "the softmax fits beside one P.V");
+    // P.V step i carries the softmax operations the plan puts there
+    auto sm_step = [&](int i, f32x4 (&sacc)[KT], u32x4 (&qh)[KS], u32x4 (&ql)[KS]) {
+        int st0 = 0;
+#pragma unroll
+        for (int k = 0; k < NSTG; ++k) {
+            const int n = sm_stage_ops<NE, X2>(k);
+            const int ns = (n + SM_CAP - 1) / SM_CAP;
+            if (i >= st0 && i < st0 + ns) {
+#pragma unroll
+                for (int o = (i - st0) * SM_CAP; o < n && o < (i - st0 + 1) * SM_CAP; ++o)
+                    sm_op(k, o, sacc, qh, ql);
+            }
+            st0 += ns;
+        }
+    };
 
     // P.V of a block (V stage vl, first VPF operands already in vb, P in
     // ph / pl) with the next block's softmax beside it: step i issues the
-    // products of operand i, the read of operand i + VPF and one softmax
-    // slice, fenced so that the order holds.
+    // products of operand i, the read of operand i + VPF and the softmax
+    // operations planned for step i, fenced so that the order holds.
     auto pv_phase = [&](const uint16_t* vl, u32x4 (&vb)[VPF], const u32x4 (&ph)[KS],
-                        const u32x4 (&pl)[KS], int bn, f32x4 (&sacc)[KT], u32x4 (&qh)[KS],
-                        u32x4 (&ql)[KS]) {
+                        const u32x4 (&pl)[KS], f32x4 (&sacc)[KT], u32x4 (&qh)[KS],
+                        u32x4 (&ql)[KS], auto&& hook) {
 #pragma unroll
         for (int i = 0; i < NPV; ++i) {
             const int k2 = i / DT, dt = i % DT;
@@ -322,9 +464,12 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
             if (i + VPF < NPV) vb[i % VPF] = rd_v(vl, i + VPF);
             oacc[dt] = mfma_bf16_16x16x32(a, ph[k2], oacc[dt]);
             if (PM == ATTN_P_BF16X2) oacc[dt] = mfma_bf16_16x16x32(a, pl[k2], oacc[dt]);
-            softmax_slice(i, bn, sacc, qh, ql);
+            sm_step(i, sacc, qh, ql);
+            hook(i);
             __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int i = NPV; i < SM_STEPS; ++i) sm_step(i, sacc, qh, ql);
     };
 
     // P of the block whose P.V comes next, and the next block's
@@ -346,9 +491,10 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     __syncthreads();
     if (head_ok) {
         f32x4 sacc[KT];
-        score_phase(ks_lds[0], vs_lds[0], sacc, vb, 1.f);
+        score_phase(ks_lds[0], vs_lds[0], sacc, vb, 1.f, [](int) {});
+        if (!is_interior(b_lo)) mask(b_lo, sacc);
 #pragma unroll
-        for (int sl = 0; sl < NSLICE; ++sl) softmax_slice(sl, b_lo, sacc, pch, pcl);
+        for (int i = 0; i < SM_STEPS; ++i) sm_step(i, sacc, pch, pcl);
     }
     __syncthreads();                             // K(b_lo) read by every wave
 
@@ -356,17 +502,38 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     // needs), then block b's P.V beside block b + 1's softmax.
     for (int b = b_lo; b < b_hi; ++b) {
         const int st = (b - b_lo) & 1;
-        // in LDS now: V(b) in vs[st], K(b + 1) in ks[st ^ 1]; P(b) in pch / pcl
-        if (b + 2 <= b_hi) dma(Kg, ks_lds[st], lane_dst, b + 2);
-        dma(Vg, vs_lds[st ^ 1], lane_dstv, b + 1);
+        // in LDS now: V(b) in vs[st], K(b + 1) in ks[st ^ 1]; P(b) in pch / pcl.
+        // K(b + 2) goes to ks[st] and V(b + 1) to vs[st ^ 1], one instruction
+        // every DMA_EVERY steps (past b_hi the K stage takes filler rows that
+        // nothing reads).
+        l2_prefetch(b + PF_AHEAD);
+        const uint16_t *kbase, *vbase;
+        uint32_t kvoff[IPW], vvoff[IPW], klds, vlds;
+        dma_plan(Kg, ks_lds[st], b + 2, kbase, kvoff, klds);
+        dma_plan(Vg, vs_lds[st ^ 1], b + 1, vbase, vvoff, vlds);
+        auto k_hook = [&](int j) {
+            if (j % DMA_EVERY == 0 && j / DMA_EVERY < IPW)
+                dma_issue(kbase, kvoff, klds, lane_dst, j / DMA_EVERY);
+        };
+        auto v_hook = [&](int j) {
+            if (j % DMA_EVERY == 0 && j / DMA_EVERY < IPW)
+                dma_issue(vbase, vvoff, vlds, lane_dstv, j / DMA_EVERY);
+        };
         if (head_ok) {
             f32x4 sacc[KT];
-            score_phase(ks_lds[st ^ 1], vs_lds[st], sacc, vb, sm_alpha);
-            pv_phase(vs_lds[st], vb, pch, pcl, b + 1, sacc, pnh, pnl);
+            score_phase(ks_lds[st ^ 1], vs_lds[st], sacc, vb, sm_alpha, k_hook);
+            if (!is_interior(b + 1)) mask(b + 1, sacc);
+            pv_phase(vs_lds[st], vb, pch, pcl, sacc, pnh, pnl, v_hook);
 #pragma unroll
             for (int k2 = 0; k2 < KS; ++k2) {
                 pch[k2] = pnh[k2];
                 pcl[k2] = pnl[k2];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < IPW; ++i) {
+                dma_issue(kbase, kvoff, klds, lane_dst, i);
+                dma_issue(vbase, vvoff, vlds, lane_dstv, i);
             }
         }
         __builtin_amdgcn_s_waitcnt(0);          // this wave's DMAs of K(b+2), V(b+1)
