@@ -7,7 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgqa_attn.so")
-SOURCES = ["api.hip", "decode.hip", "prefill.hip", "cache_write.hip"]
+SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill512.hip", "cache_write.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -22,8 +22,8 @@ FLAGS = [
 # loops must unroll fully (a step index that stays dynamic would put the
 # register arrays it indexes into scratch memory), beyond clang's default
 # size limit for unroll pragmas
-EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form",
-                         "-mllvm", "-pragma-unroll-threshold=1000000"]}
+_PROMPT = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-pragma-unroll-threshold=1000000"]
+EXTRA = {"prefill.hip": _PROMPT, "prefill512.hip": _PROMPT}
 NOISE = "is not a recognized feature for this target"
 
 

@@ -158,11 +158,12 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         for (int st = 0; st < QST; ++st) {
             u32x4 z = {0u, 0u, 0u, 0u};
             qreg[st] = (row_ok && head_ok) ? ld16(qrow + 32 * st) : z;
-            // Q lives in AGPRs (the products read their B operand from
-            // there), which leaves the VGPRs to the accumulators and to the
-            // operand reads in flight
-            asm volatile("" : "+a"(qreg[st]));
         }
+        // Q lives in AGPRs (the products read their B operand from there),
+        // which leaves the VGPRs to the accumulators and to the operand reads
+        // in flight; all loads are issued before the first move
+#pragma unroll
+        for (int st = 0; st < QST; ++st) asm volatile("" : "+a"(qreg[st]));
     }
 
     const uint16_t* Kg = kc + (size_t)g * cap * D;
@@ -574,20 +575,18 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                           const uint16_t* vc, int pos0, int n_rows, int Hq,
                           int Hkv, int D, int cap, int ring, int window,
                           float scale, int p_mode, hipStream_t stream) {
+    if (D == 512)
+        return launch_prefill_512(out, q, kc, vc, pos0, n_rows, Hq, Hkv, cap, ring, window,
+                                  scale, p_mode, stream);
     const int G = Hq / Hkv;
     const int HG = (G + 3) / 4;
     const float c = scale * ATTN_LOG2E;
     dim3 grid(((n_rows + 15) / 16) * Hkv * HG);
-#define PREFILL_LAUNCH(DD, PMV)                                                        \
-    prefill_kernel<DD, PMV><<<grid, 256, 0, stream>>>(out, q, kc, vc, pos0, n_rows, Hq, \
-                                                      Hkv, G, HG, cap, ring, window, c)
-    if (D == 256) {
-        if (p_mode == ATTN_P_BF16X2) PREFILL_LAUNCH(256, ATTN_P_BF16X2);
-        else PREFILL_LAUNCH(256, ATTN_P_BF16);
-    } else {
-        if (p_mode == ATTN_P_BF16X2) PREFILL_LAUNCH(512, ATTN_P_BF16X2);
-        else PREFILL_LAUNCH(512, ATTN_P_BF16);
-    }
-#undef PREFILL_LAUNCH
+    if (p_mode == ATTN_P_BF16X2)
+        prefill_kernel<256, ATTN_P_BF16X2><<<grid, 256, 0, stream>>>(
+            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c);
+    else
+        prefill_kernel<256, ATTN_P_BF16><<<grid, 256, 0, stream>>>(
+            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c);
     return hipGetLastError();
 }
