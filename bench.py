@@ -188,7 +188,7 @@ def main():
     flops_prompt = causal_pairs(n, w.window) * Hq * 4 * D        # algorithmic
     flops_launch = flops_prompt / n_chunks
     pf_tflops = flops_launch / (pf_launch_ms * 1e-3) / 1e12
-    src = os.path.join(ROOT, "global_gqa_attention_window_amd", "csrc", "prefill.hip")
+    src = os.path.join(ROOT, "global_gqa_attention_window_amd", "csrc", "prefill512.hip")
     traffic = traffic_from_profile(src)
     dec_bytes = 2 * Hkv * dcap * D * 2 + 2 * Hq * D * 2           # K+V read, q, out
     dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
@@ -210,7 +210,7 @@ def main():
                    "prompt_tokens": n, "chunk_rows": ch, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "p_mode": "bf16x2", "window": 0,
                    "decode_cache_keys": dcap, "seed": w.seed},
-        "roofline": {"kernel": "prefill_kernel<512,bf16x2>", "bound": "mfma",
+        "roofline": {"kernel": "prefill_pair_kernel<bf16x2>", "bound": "mfma",
                      "achieved": round(pf_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pf_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
