@@ -116,6 +116,10 @@ void decode_partial_kernel(const uint16_t* __restrict__ q,
             u32x4 z = {0u, 0u, 0u, 0u};
             qreg[st] = hv ? ld16(qrow + 32 * st + 8 * grp) : z;
         }
+        // Q lives in AGPRs (the score products read their B operand there),
+        // leaving the VGPRs to the accumulator and two tiles of V
+#pragma unroll
+        for (int st = 0; st < QST; ++st) asm volatile("" : "+a"(qreg[st]));
     }
 
     f32x4 acc[SPANS][8];
@@ -129,19 +133,23 @@ void decode_partial_kernel(const uint16_t* __restrict__ q,
     // of its LDS row, so the eight lanes of one LDS read phase (eight rows,
     // same chunk) hit eight different bank groups.  The slot is clamped in
     // range; a key that is not attended is masked out of the scores.
+    // (issued from asm, one instruction at a time between the score
+    // products: the compiler then adds no wait for it before the LDS reads
+    // of the other stage; the tile loop waits for it explicitly)
+    auto load_k_one = [&](int sb, int stage, int i) {
+        const int row = i * RPD + lane / LPR;
+        const int slot = min(sb + row, cap - 1);
+        const int chunk = (lane % LPR) ^ (row & 7);
+        dma16_asm(K + (size_t)slot * D + chunk * 8, lds_addr(&ks[stage][i * RPD * D]));
+    };
     auto load_k = [&](int sb, int stage) {
 #pragma unroll
-        for (int i = 0; i < TILE / RPD; ++i) {
-            const int row = i * RPD + lane / LPR;
-            const int slot = min(sb + row, cap - 1);
-            const int chunk = (lane % LPR) ^ (row & 7);
-            ATTN_DMA16(K + (size_t)slot * D + chunk * 8, &ks[stage][i * RPD * D]);
-        }
+        for (int i = 0; i < TILE / RPD; ++i) load_k_one(sb, stage, i);
     };
     // V rows (sb + 4 grp + r), d = 128 sp + 8 col .. +7: sixteen lanes read
     // 256 contiguous bytes of one row per load
-    u32x4 vcur[4][SPANS];
-    u32x4 vnxt[4][SPANS];
+    u32x4 vbuf0[4][SPANS];
+    u32x4 vbuf1[4][SPANS];
     auto load_v = [&](int sb, u32x4 (&dst)[4][SPANS]) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -155,21 +163,30 @@ void decode_partial_kernel(const uint16_t* __restrict__ q,
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    load_k(slot0 + tt_lo * TILE, 0);
-    load_v(slot0 + tt_lo * TILE, vcur);
-    for (int tt = tt_lo; tt <= tt_hi; ++tt) {
+    // One 16-key tile; V of this tile in vc, the next tile's V goes to vn.
+    static_assert(TILE / RPD == QST, "one K DMA instruction per score product");
+    auto tile = [&](int tt, const u32x4 (&vc)[4][SPANS], u32x4 (&vn)[4][SPANS]) {
         const int stage = (tt - tt_lo) & 1;
         const int sb = slot0 + tt * TILE;
+        const bool more = tt < tt_hi;
         // K(tt) in LDS and V(tt) in registers have landed
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (tt < tt_hi) load_k(sb + TILE, stage ^ 1);
+        if (more) load_v(sb + TILE, vn);         // in flight through this tile
 
+        // scores: the two halves of the head dim accumulate separately (two
+        // independent product chains) and are added at the end; the next
+        // tile's K moves in beside them, one DMA instruction per product
         const uint16_t* kt = &ks[stage][0];
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < QST; ++st)
-            sc = mfma_bf16_16x16x32(ld16(kt + col * D + 8 * ((4 * st + grp) ^ (col & 7))), qreg[st], sc);
+        for (int st = 0; st < QST; ++st) {
+            const u32x4 kop = ld16(kt + col * D + 8 * ((4 * st + grp) ^ (col & 7)));
+            if (st < QST / 2) sa = mfma_bf16_16x16x32(kop, qreg[st], sa);
+            else sb2 = mfma_bf16_16x16x32(kop, qreg[st], sb2);
+            if (more) load_k_one(sb + TILE, stage ^ 1, st);
+        }
+        const f32x4 sc = sa + sb2;
 
         float tv[4];
         uint32_t vmask[4], vsel[4];
@@ -184,10 +201,27 @@ void decode_partial_kernel(const uint16_t* __restrict__ q,
             vmask[i] = ok ? 0xFFFF0000u : 0u;
             vsel[i] = ok ? 0x01000C0Cu : 0x0C0C0C0Cu;
         }
+        // Reference maximum.  Decode keeps p in fp32 and never rounds it
+        // against the maximum, so the maximum only keeps exp2 in range: it
+        // moves (and the accumulator is rescaled) only when a tile's maximum
+        // passes it by more than 8, so p <= 2^8 and a run's row sum stays
+        // below 2^18, far inside fp32; the partial carries the reference it
+        // used, which the merge takes as the chunk maximum.
         mx = xmax4(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);   // 0 when m_run = -inf
+        const bool grow = mx > m_run + 8.f;       // first attended tile: m_run = -inf
+        if (__any(grow)) {
+            const float m_new = grow ? mx : m_run;
+            // 0 when growing from -inf; exactly 1 for a lane that keeps its
+            // reference (also one still at -inf, where the difference is NaN)
+            const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int sp = 0; sp < SPANS; ++sp)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[sp][j] *= alpha;
+            m_run = m_new;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
         float pv[4];
         float psum = 0.f;
 #pragma unroll
@@ -195,20 +229,12 @@ void decode_partial_kernel(const uint16_t* __restrict__ q,
             pv[i] = fast_exp2(tv[i] - m_use);              // 0 for masked keys
             psum += pv[i];
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (tt < tt_hi) load_v(sb + TILE, vnxt);      // in flight during P.V
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int sp = 0; sp < SPANS; ++sp)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[sp][j] *= alpha;
-        }
+        l_run += psum;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
 #pragma unroll
             for (int sp = 0; sp < SPANS; ++sp) {
-                const u32x4 w = vcur[r][sp];
+                const u32x4 w = vc[r][sp];
                 const float p = pv[r];
                 const uint32_t sl = vsel[r], mk = vmask[r];
 #define LO(x) __uint_as_float(__builtin_amdgcn_perm(0u, (x), sl))
@@ -225,10 +251,16 @@ void decode_partial_kernel(const uint16_t* __restrict__ q,
 #undef HI
             }
         }
+    };
+
+    load_k(slot0 + tt_lo * TILE, 0);
+    load_v(slot0 + tt_lo * TILE, vbuf0);
+    for (int tt = tt_lo; tt <= tt_hi; ++tt) {
+        tile(tt, vbuf0, vbuf1);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int sp = 0; sp < SPANS; ++sp) vcur[r][sp] = vnxt[r][sp];
+            for (int sp = 0; sp < SPANS; ++sp) vbuf0[r][sp] = vbuf1[r][sp];
     }
 
     const float l_tot = xsum4(l_run);
