@@ -86,10 +86,25 @@ def key_valid(positions: np.ndarray, t: int, window: int) -> np.ndarray:
     return ok
 
 
-def prefill_key_range(t: int, window: int) -> tuple[int, int]:
-    """First and last key position a prompt row at position t attends."""
+def prefill_key_range(t: int, window: int, hi: int | None = None) -> tuple[int, int]:
+    """First and last key position a prompt row at position t attends.
+
+    hi is the row's last key (PR #975 commit body: the prompt attention takes
+    each row's last key, its own position for text rows, so an image's rows
+    see each other on sliding layers); None means the row's own position.
+    The window's first key stays t - W + 1.
+    """
     lo = max(0, t - window + 1) if window > 0 else 0
-    return lo, t
+    return lo, (t if hi is None else hi)
+
+
+def clamp_last_key(last_key, pos0: int, n_rows: int) -> np.ndarray:
+    """Last keys of the rows of one call, clamped to [own position, last row]:
+    a row never attends fewer keys than causal, nor a key past the call's
+    last row (the cache holds nothing later)."""
+    t = pos0 + np.arange(n_rows)
+    lk = np.asarray(last_key, dtype=np.int64)
+    return np.minimum(np.maximum(lk, t), pos0 + n_rows - 1)
 
 
 # --------------------------------------------------------------------------
@@ -256,12 +271,14 @@ def decode_chunked(q_bits, k_bits, v_bits, pos, n_kv_heads: int, ring: int,
 
 def prefill(q_bits, k_bits, v_bits, pos0: int, n_kv_heads: int, window: int,
             scale: float, p_mode: int, kb: int, rows=None, heads=None,
-            row_batch: int = 256):
+            row_batch: int = 256, last_key=None):
     """Prompt rows at positions pos0 + i against keys by absolute position.
 
     q [n][Hq][D]; k, v [n_pos][Hkv][D] with row p the key/value at position
     p (n_pos > pos0 + n - 1).  rows / heads select the outputs to compute
-    (default all).  Returns dict(o, r, bits) of shape [len(rows)][len(heads)][D].
+    (default all).  last_key [n] (optional): each row's last key position,
+    used as given (callers clamp with clamp_last_key).  Returns dict(o, r,
+    bits) of shape [len(rows)][len(heads)][D].
     """
     q = q_bits if q_bits.dtype == np.float64 else as_f64(q_bits)
     k = k_bits if k_bits.dtype == np.float64 else as_f64(k_bits)
@@ -279,9 +296,10 @@ def prefill(q_bits, k_bits, v_bits, pos0: int, n_kv_heads: int, window: int,
         rr = rows[sel]
         t = pos0 + rr
         lo = np.array([prefill_key_range(int(x), window)[0] for x in t])
-        j0, j1 = int(lo.min()), int(t.max())
+        hi = t if last_key is None else np.asarray(last_key, dtype=np.int64)[rr]
+        j0, j1 = int(lo.min()), int(hi.max())
         j = np.arange(j0, j1 + 1)
-        mask = (j[None, :] >= lo[:, None]) & (j[None, :] <= t[:, None])
+        mask = (j[None, :] >= lo[:, None]) & (j[None, :] <= hi[:, None])
         blk = j // kb
         for hi, h in enumerate(heads):
             g = int(h) // G

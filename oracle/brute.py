@@ -102,17 +102,19 @@ def decode_row(q, kcache, vcache, t: int, ring: int, window: int, scale: float):
 
 
 def prefill_row(q, keys, values, t: int, window: int, scale: float,
-                p_mode: int, kb: int):
-    """q [D]; keys, values [n_pos][D] by absolute position; returns [D]."""
+                p_mode: int, kb: int, hi: int | None = None):
+    """q [D]; keys, values [n_pos][D] by absolute position; returns [D].
+    hi: the row's last key (default its own position t)."""
     D = len(q)
     lo = max(0, t - window + 1) if window else 0
+    hi = t if hi is None else hi
     m = -math.inf
     l = 0.0
     acc = [0.0] * D
     b = lo // kb
-    while b * kb <= t:
+    while b * kb <= hi:
         first = max(lo, b * kb)
-        last = min(t, b * kb + kb - 1)
+        last = min(hi, b * kb + kb - 1)
         s = [scale * _dot(q, keys[j]) for j in range(first, last + 1)]
         m_new = max(m, max(s))
         alpha = math.exp(m - m_new) if m != -math.inf else 0.0
