@@ -104,7 +104,8 @@ def attn_decode(out, q, k_cache, v_cache, pos, n_seq, n_q_heads, n_kv_heads,
 def attn_prefill(out, q, k_cache, v_cache, pos0, n_rows, n_q_heads, n_kv_heads,
                  head_dim, cache_cap, ring, window, scale, p_mode,
                  last_key=None, stream=None) -> None:
-    """out/q [n_rows][Hq][D], caches [Hkv][cap][D] (bf16)."""
+    """out/q [n_rows][Hq][D], caches [Hkv][cap][D] (bf16); last_key: None
+    (causal) or a device int32 [n_rows] of each row's last key position."""
     st = _lib.attn_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), pos0,
                            n_rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring,
                            window, float(scale), p_mode, _ptr(last_key), _stream(stream))

@@ -113,7 +113,6 @@ int attn_prefill(void* out, const void* q, const void* k_cache,
     int st = check_heads(n_q_heads, n_kv_heads, head_dim);
     if (st != ATTN_OK) return st;
     if (p_mode != ATTN_P_BF16 && p_mode != ATTN_P_BF16X2) return ATTN_E_P_MODE;
-    if (last_key) return ATTN_E_UNSUPPORTED;
     if (n_rows < 0 || pos0 < 0 || (ring != 0 && ring != 1) || !isfinite(scale))
         return ATTN_E_RANGE;
     if (cache_cap < 1) return ATTN_E_CACHE;
@@ -131,11 +130,12 @@ int attn_prefill(void* out, const void* q, const void* k_cache,
     if (!out || !q || !k_cache || !v_cache) return ATTN_E_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return ATTN_E_ALIGN;
+    if (last_key && (reinterpret_cast<uintptr_t>(last_key) & 3u)) return ATTN_E_ALIGN;
     hipError_t e = launch_prefill(
         static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
         static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
         pos0, n_rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring, window,
-        scale, p_mode, static_cast<hipStream_t>(stream));
+        scale, p_mode, last_key, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 

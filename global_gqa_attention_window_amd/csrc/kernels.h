@@ -20,13 +20,14 @@ int prefill_key_block(int D, int p_mode);
 hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                           const uint16_t* vc, int pos0, int n_rows, int Hq,
                           int Hkv, int D, int cap, int ring, int window,
-                          float scale, int p_mode, hipStream_t stream);
+                          float scale, int p_mode, const int32_t* last_key,
+                          hipStream_t stream);
 
 // head dim 512 (prefill512.hip)
 hipError_t launch_prefill_512(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                               const uint16_t* vc, int pos0, int n_rows, int Hq, int Hkv,
                               int cap, int ring, int window, float scale, int p_mode,
-                              hipStream_t stream);
+                              const int32_t* last_key, hipStream_t stream);
 
 hipError_t launch_cache_write(uint16_t* kc, uint16_t* vc, const uint16_t* k,
                               const uint16_t* v, int pos0, int n_rows, int Hkv,

@@ -93,7 +93,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                     int pos0, int n_rows, int Hq, int Hkv, int G, int HG, int cap,
-                    int ring, int window, float c) {
+                    int ring, int window, float c,
+                    const int32_t* __restrict__ last_key) {
     constexpr int KB = PrefillCfg<D>::KB;
     constexpr int KPADP = 16;                // K padding per row (pair at 256)
     constexpr int VPADP = 16;                // V padding per row (pair at 256)
@@ -142,13 +143,23 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int t_last = pos0 + r0 + nvalid - 1;
     const int lo_tile = window > 0 ? max(0, t_first - window + 1) : 0;
     const int lo_last = window > 0 ? max(0, t_last - window + 1) : 0;
-    const int hi_tile = t_last;
-    const int b_lo = lo_tile / KB;
-    const int b_hi = hi_tile / KB;
-
     const bool row_ok = col < nvalid;
     const int t_row = pos0 + r0 + col;
     const int lo_row = window > 0 ? max(0, t_row - window + 1) : 0;
+    // each row's last key: its own position, or last_key's value clamped to
+    // [own position, the chunk's last row]; the tile reads keys up to the
+    // largest of its rows' last keys (a wave-uniform value)
+    int t_hi = t_row;
+    if (last_key != nullptr && row_ok)
+        t_hi = min(max((int)last_key[r0 + col], t_row), pos0 + n_rows - 1);
+    int hi_m = row_ok ? t_hi : t_first;
+    hi_m = max(hi_m, __shfl_xor(hi_m, 1));
+    hi_m = max(hi_m, __shfl_xor(hi_m, 2));
+    hi_m = max(hi_m, __shfl_xor(hi_m, 4));
+    hi_m = max(hi_m, __shfl_xor(hi_m, 8));
+    const int hi_tile = __builtin_amdgcn_readfirstlane(hi_m);
+    const int b_lo = lo_tile / KB;
+    const int b_hi = hi_tile / KB;
 
     // Q^T operand: lane holds Q[row col][head h][32 st + 8 grp .. +7]
     u32x4 qreg[QST];
@@ -257,7 +268,8 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int vofs = row_pos<D, VPADP>(4 * grp + (col >> 2)) + 4 * (col & 3);
 
     // a block needs no per-key mask when every row of the tile attends all
-    // of its keys; the others mask keys outside [lo_row, t_row] with -inf
+    // of its keys (a row's last key is never before its own position); the
+    // others mask keys outside [lo_row, t_hi] with -inf
     auto is_interior = [&](int b) {
         const int p0 = b * KB;
         return p0 >= lo_last && p0 + KB - 1 <= t_first;
@@ -269,7 +281,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int p = p0 + 16 * kt + 4 * grp + i;
-                sacc[kt][i] = (p >= lo_row && p <= t_row) ? sacc[kt][i] : -INFINITY;
+                sacc[kt][i] = (p >= lo_row && p <= t_hi) ? sacc[kt][i] : -INFINITY;
             }
     };
 
@@ -574,19 +586,20 @@ int prefill_key_block(int D, int p_mode) {
 hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                           const uint16_t* vc, int pos0, int n_rows, int Hq,
                           int Hkv, int D, int cap, int ring, int window,
-                          float scale, int p_mode, hipStream_t stream) {
+                          float scale, int p_mode, const int32_t* last_key,
+                          hipStream_t stream) {
     if (D == 512)
         return launch_prefill_512(out, q, kc, vc, pos0, n_rows, Hq, Hkv, cap, ring, window,
-                                  scale, p_mode, stream);
+                                  scale, p_mode, last_key, stream);
     const int G = Hq / Hkv;
     const int HG = (G + 3) / 4;
     const float c = scale * ATTN_LOG2E;
     dim3 grid(((n_rows + 15) / 16) * Hkv * HG);
     if (p_mode == ATTN_P_BF16X2)
         prefill_kernel<256, ATTN_P_BF16X2><<<grid, 256, 0, stream>>>(
-            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c);
+            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key);
     else
         prefill_kernel<256, ATTN_P_BF16><<<grid, 256, 0, stream>>>(
-            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c);
+            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key);
     return hipGetLastError();
 }

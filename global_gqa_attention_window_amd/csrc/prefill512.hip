@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_pair_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                          const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                          int pos0, int n_rows, int Hq, int Hkv, int G, int HG, int cap,
-                         int ring, int window, float c) {
+                         int ring, int window, float c,
+                         const int32_t* __restrict__ last_key) {
     constexpr int D = P5_D, KB = P5_KB, HD = P5_H;
     constexpr bool X2 = PM == ATTN_P_BF16X2;
     constexpr int KT = KB / 16;              // 16-key score tiles per block
@@ -131,12 +132,23 @@ void prefill_pair_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict_
     const int t_last = pos0 + r0 + nvalid - 1;
     const int lo_tile = window > 0 ? max(0, t_first - window + 1) : 0;
     const int lo_last = window > 0 ? max(0, t_last - window + 1) : 0;
-    const int hi_tile = t_last;
-    const int b_lo = lo_tile / KB;
-    const int b_hi = hi_tile / KB;
     const bool row_ok = col < nvalid;
     const int t_row = pos0 + r0 + col;
     const int lo_row = window > 0 ? max(0, t_row - window + 1) : 0;
+    // each row's last key: its own position, or last_key's value clamped to
+    // [own position, the chunk's last row]; the tile reads keys up to the
+    // largest of its rows' last keys (a wave-uniform value)
+    int t_hi = t_row;
+    if (last_key != nullptr && row_ok)
+        t_hi = min(max((int)last_key[r0 + col], t_row), pos0 + n_rows - 1);
+    int hi_m = row_ok ? t_hi : t_first;
+    hi_m = max(hi_m, __shfl_xor(hi_m, 1));
+    hi_m = max(hi_m, __shfl_xor(hi_m, 2));
+    hi_m = max(hi_m, __shfl_xor(hi_m, 4));
+    hi_m = max(hi_m, __shfl_xor(hi_m, 8));
+    const int hi_tile = __builtin_amdgcn_readfirstlane(hi_m);
+    const int b_lo = lo_tile / KB;
+    const int b_hi = hi_tile / KB;
 
     // Q^T operands of both heads over this wave's half, in AGPRs (the
     // products read their B operand there): Q[row col][head][256 dh + 32 st
@@ -239,11 +251,13 @@ void prefill_pair_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict_
         return lds_read_tr16(vl + vofs + half * 16 * ROW + 16 * dt);
     };
 
+    // a block needs no per-key mask when every row of the tile attends all of
+    // its keys (a row's last key is never before its own position)
     auto is_interior = [&](int b) {
         const int p0 = b * KB;
         return p0 >= lo_last && p0 + KB - 1 <= t_first;
     };
-    // keys outside [lo_row, t_row] score -inf; applied to the own partial
+    // keys outside [lo_row, t_hi] score -inf; applied to the own partial
     // (-inf plus the partner's finite or -inf partial stays -inf)
     auto mask = [&](int b, f32x4 (&sacc)[2][KT]) {
         const int p0 = b * KB;
@@ -252,7 +266,7 @@ void prefill_pair_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict_
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int p = p0 + 16 * kt + 4 * grp + i;
-                const bool okp = p >= lo_row && p <= t_row;
+                const bool okp = p >= lo_row && p <= t_hi;
 #pragma unroll
                 for (int k = 0; k < 2; ++k) sacc[k][kt][i] = okp ? sacc[k][kt][i] : -INFINITY;
             }
@@ -565,16 +579,16 @@ void prefill_pair_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict_
 hipError_t launch_prefill_512(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                               const uint16_t* vc, int pos0, int n_rows, int Hq, int Hkv,
                               int cap, int ring, int window, float scale, int p_mode,
-                              hipStream_t stream) {
+                              const int32_t* last_key, hipStream_t stream) {
     const int G = Hq / Hkv;
     const int HG = (G + 3) / 4;
     const float c = scale * ATTN_LOG2E;
     dim3 grid(((n_rows + 15) / 16) * Hkv * HG);
     if (p_mode == ATTN_P_BF16X2)
         prefill_pair_kernel<ATTN_P_BF16X2><<<grid, 256, 0, stream>>>(
-            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c);
+            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key);
     else
         prefill_pair_kernel<ATTN_P_BF16><<<grid, 256, 0, stream>>>(
-            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c);
+            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key);
     return hipGetLastError();
 }

@@ -141,8 +141,15 @@ int attn_decode(void* out, const void* q, const void* k_cache,
  *   ring      0 linear (pos0 + n_rows <= cap), 1 ring (0 < W <= cap and
  *             cap >= W + n_rows - 1, so no row's keys are overwritten)
  *   p_mode    ATTN_P_BF16 or ATTN_P_BF16X2
- *   last_key  must be NULL (per-row key bounds are not implemented yet:
- *             non-NULL returns ATTN_E_UNSUPPORTED)
+ *   last_key  NULL: each row's last key is its own position (causal).  Or
+ *             device int32 [n_rows], 4-byte aligned: the last key position
+ *             row r attends (PR #975 commit body: the prompt attention takes
+ *             each row's last key, its own position for text rows; PR #1183
+ *             body: an image's rows see each other on sliding layers through
+ *             the last-key rows).  Each value is clamped to [pos0 + r,
+ *             pos0 + n_rows - 1]: never fewer keys than causal, never a key
+ *             the chunk has not written.  The window's first key stays
+ *             pos0 + r - W + 1.  Values are read on the device, not checked.
  */
 int attn_prefill(void* out, const void* q, const void* k_cache,
                  const void* v_cache, int pos0, int n_rows, int n_q_heads,

@@ -134,3 +134,48 @@ def prefill_inputs(w: Workload, n_rows: int | None = None, seed: int | None = No
     k = randn_bf16_bits(rng, (n, w.Hkv, w.D))
     v = randn_bf16_bits(rng, (n, w.Hkv, w.D))
     return q, k, v
+
+
+def image_spans(rng: np.random.Generator, n: int, n_images: int = 6, min_len: int = 64,
+                max_len: int = 280) -> list[tuple[int, int]]:
+    """Row spans [a, b] (inclusive, ascending, disjoint) of n_images images in
+    an n-row prompt: lengths uniform in [min_len, max_len] (an image takes up
+    to 280 rows), text between them split at uniform random cuts."""
+    lens = rng.integers(min_len, max_len + 1, n_images)
+    text = n - int(lens.sum())
+    if text < 0:
+        raise ValueError("images longer than the prompt")
+    gaps = np.diff(np.concatenate([[0], np.sort(rng.integers(0, text + 1, n_images)),
+                                   [text]]))
+    spans, p = [], 0
+    for i in range(n_images):
+        p += int(gaps[i])
+        spans.append((p, p + int(lens[i]) - 1))
+        p += int(lens[i])
+    return spans
+
+
+def image_span_last_keys(pos0: int, n: int, spans) -> np.ndarray:
+    """Each row's last key: its own position, or its image's last position
+    for rows inside a span (spans in absolute positions)."""
+    t = pos0 + np.arange(n, dtype=np.int64)
+    lk = t.copy()
+    for a, b in spans:
+        inside = (t >= a) & (t <= b)
+        lk[inside] = b
+    return lk
+
+
+def chunk_starts(n: int, max_rows: int, spans) -> list[int]:
+    """Starts of prompt chunks of up to max_rows rows that never cut an
+    image: a cut inside a span moves to the span's start, or past its end
+    when the chunk itself starts there (that chunk is then longer)."""
+    starts, s = [], 0
+    while s < n:
+        starts.append(s)
+        e = min(n, s + max_rows)
+        for a, b in spans:
+            if a < e <= b:
+                e = a if a > s else b + 1
+        s = e
+    return starts

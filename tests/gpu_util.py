@@ -39,8 +39,10 @@ def run_decode(ga, q, k, v, pos, Hkv, ring, window, scale, ws_pad=0):
 
 
 def run_prefill(ga, q, k, v, Hkv, cap, ring, window, scale, p_mode, chunk,
-                pos0=0, caches=None):
-    """Prompt rows pos0.. in chunks: cache write, then attention, per chunk."""
+                pos0=0, caches=None, last_key=None, starts=None):
+    """Prompt rows pos0.. in chunks: cache write, then attention, per chunk.
+    Chunks of `chunk` rows, or starting at `starts` (row indices) when given.
+    last_key [n] (absolute positions, optional) is passed per chunk as given."""
     n, Hq, D = q.shape
     if caches is None:
         kc = torch.zeros((Hkv, cap, D), dtype=torch.int16, device=DEV)
@@ -49,10 +51,13 @@ def run_prefill(ga, q, k, v, Hkv, cap, ring, window, scale, p_mode, chunk,
         kc, vc = caches
     qd, kd, vd = up(q), up(k[pos0:pos0 + n]), up(v[pos0:pos0 + n])
     out = torch.empty((n, Hq, D), dtype=torch.int16, device=DEV)
-    for r0 in range(0, n, chunk):
-        m = min(chunk, n - r0)
+    lkd = None if last_key is None else up(np.asarray(last_key, dtype=np.int32))
+    starts = list(range(0, n, chunk)) if starts is None else list(starts)
+    for r0, r1 in zip(starts, starts[1:] + [n]):
+        m = r1 - r0
         ga.attn_cache_write(kc, vc, kd[r0:r0 + m], vd[r0:r0 + m], pos0 + r0, m, Hkv, D,
                             cap, ring)
         ga.attn_prefill(out[r0:r0 + m], qd[r0:r0 + m], kc, vc, pos0 + r0, m, Hq, Hkv, D,
-                        cap, ring, window, scale, p_mode)
+                        cap, ring, window, scale, p_mode,
+                        last_key=None if lkd is None else lkd[r0:r0 + m])
     return down(out), (kc, vc)

@@ -134,7 +134,7 @@ def test_decode_zero_streams_is_a_no_op(ga):
     (dict(out=None), "ATTN_E_NULL"), (dict(k=None), "ATTN_E_NULL"),
     (dict(D=64), "ATTN_E_HEAD_DIM"), (dict(Hq=30), "ATTN_E_GQA"),
     (dict(p_mode=P_FP32), "ATTN_E_P_MODE"), (dict(p_mode=7), "ATTN_E_P_MODE"),
-    (dict(last=P), "ATTN_E_UNSUPPORTED"),
+    (dict(last=P + 2), "ATTN_E_ALIGN"),
     (dict(ring=1, window=0), "ATTN_E_WINDOW"), (dict(window=1153), "ATTN_E_WINDOW"),
     (dict(window=-3), "ATTN_E_WINDOW"),
     (dict(cap=1150), "ATTN_E_CACHE"),              # ring < window + rows - 1
