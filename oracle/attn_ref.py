@@ -220,6 +220,33 @@ def decode(q_bits, k_bits, v_bits, pos, n_kv_heads: int, ring: int,
     return dict(o=o, r=r, bits=bf16.bits_from_f64(o))
 
 
+def decode_rows(q_bits, k_bits, v_bits, pos, n_kv_heads: int, ring: int,
+                window: int, scale: float):
+    """A decode window of R rows per stream: row r of stream s sits at
+    position pos[s] + r and is an ordinary decode row of that position
+    (PR #975 decode commits: a key head's query heads and several decode rows
+    share one 16-row tile; every row keeps its bits at any window width, so
+    a row's value does not depend on the rows beside it).
+
+    q [S][R][Hq][D]; caches [S][Hkv][cap][D] hold every row's key and value
+    (written before attention).  A ring must still hold the window of the
+    first row after the later rows' writes: window >= 1 and cap >= window +
+    R - 1.  Returns dict(o, r, bits) with o, r [S][R][Hq][D].
+    """
+    S, R = q_bits.shape[:2]
+    cap = k_bits.shape[2]
+    if ring and (window < 1 or cap < window + R - 1):
+        raise ValueError("a ring needs window >= 1 and cap >= window + rows - 1")
+    pos = np.asarray(pos, dtype=np.int64)
+    o = np.zeros(q_bits.shape)
+    r = np.zeros(q_bits.shape)
+    for i in range(R):
+        res = decode(q_bits[:, i], k_bits, v_bits, pos + i, n_kv_heads, ring, window, scale)
+        o[:, i] = res["o"]
+        r[:, i] = res["r"]
+    return dict(o=o, r=r, bits=bf16.bits_from_f64(o))
+
+
 def decode_chunked(q_bits, k_bits, v_bits, pos, n_kv_heads: int, ring: int,
                    window: int, scale: float, chunk: int = DECODE_CHUNK):
     """Decode by chunk partials merged in chunk order (float64 values).
