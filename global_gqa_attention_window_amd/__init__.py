@@ -26,6 +26,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 ATTN_OK = 0
 ATTN_P_FP32, ATTN_P_BF16, ATTN_P_BF16X2 = 0, 1, 2
 ATTN_DECODE_CHUNK = 256
+ATTN_DECODE_MAX_ROWS = 16
 
 _c_int, _c_void_p, _c_float, _c_size_t = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
 
@@ -33,6 +34,11 @@ _lib.attn_decode_workspace_bytes.restype = _c_size_t
 _lib.attn_decode_workspace_bytes.argtypes = [_c_int] * 4
 _lib.attn_decode.restype = _c_int
 _lib.attn_decode.argtypes = ([_c_void_p] * 5 + [_c_int] * 7 + [_c_float, _c_void_p, _c_size_t, _c_void_p])
+_lib.attn_decode_rows_workspace_bytes.restype = _c_size_t
+_lib.attn_decode_rows_workspace_bytes.argtypes = [_c_int] * 5
+_lib.attn_decode_rows.restype = _c_int
+_lib.attn_decode_rows.argtypes = ([_c_void_p] * 5 + [_c_int] * 8 +
+                                  [_c_float, _c_void_p, _c_size_t, _c_void_p])
 _lib.attn_prefill.restype = _c_int
 _lib.attn_prefill.argtypes = ([_c_void_p] * 4 + [_c_int] * 8 + [_c_float, _c_int, _c_void_p, _c_void_p])
 _lib.attn_cache_write.restype = _c_int
@@ -82,6 +88,12 @@ def attn_decode_workspace_bytes(n_seq: int, n_q_heads: int, head_dim: int, cache
     return int(_lib.attn_decode_workspace_bytes(n_seq, n_q_heads, head_dim, cache_cap))
 
 
+def attn_decode_rows_workspace_bytes(n_seq: int, rows: int, n_q_heads: int, head_dim: int,
+                                     cache_cap: int) -> int:
+    return int(_lib.attn_decode_rows_workspace_bytes(n_seq, rows, n_q_heads, head_dim,
+                                                     cache_cap))
+
+
 def attn_prefill_key_block(head_dim: int, p_mode: int) -> int:
     kb = int(_lib.attn_prefill_key_block(head_dim, p_mode))
     _ok(min(kb, 0), "attn_prefill_key_block")
@@ -99,6 +111,20 @@ def attn_decode(out, q, k_cache, v_cache, pos, n_seq, n_q_heads, n_kv_heads,
                           window, float(scale), _ptr(workspace), int(workspace_bytes),
                           _stream(stream))
     _ok(st, "attn_decode")
+
+
+def attn_decode_rows(out, q, k_cache, v_cache, pos, n_seq, rows, n_q_heads, n_kv_heads,
+                     head_dim, cache_cap, ring, window, scale, workspace,
+                     workspace_bytes=None, stream=None) -> None:
+    """out/q [S][rows][Hq][D], caches [S][Hkv][cap][D] (bf16), pos int32 [S]
+    (the first row's position)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.attn_decode_rows(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pos),
+                               n_seq, rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring,
+                               window, float(scale), _ptr(workspace), int(workspace_bytes),
+                               _stream(stream))
+    _ok(st, "attn_decode_rows")
 
 
 def attn_prefill(out, q, k_cache, v_cache, pos0, n_rows, n_q_heads, n_kv_heads,

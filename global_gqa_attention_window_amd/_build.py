@@ -16,14 +16,14 @@ FLAGS = [
     # no packed fp32 instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# per-source extras for the prompt kernel: its matrix-core accumulators stay
-# in ordinary VGPRs (Q sits in AGPRs instead), so rescaling them needs no
-# copies between accumulation and arithmetic registers; and its fenced step
-# loops must unroll fully (a step index that stays dynamic would put the
-# register arrays it indexes into scratch memory), beyond clang's default
-# size limit for unroll pragmas
+# per-source extras for the prompt and decode-window kernels: their
+# matrix-core accumulators stay in ordinary VGPRs (Q sits in AGPRs instead),
+# so rescaling them needs no copies between accumulation and arithmetic
+# registers; and their step loops must unroll fully (a step index that stays
+# dynamic would put the register arrays it indexes into scratch memory),
+# beyond clang's default size limit for unroll pragmas
 _PROMPT = ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-pragma-unroll-threshold=1000000"]
-EXTRA = {"prefill.hip": _PROMPT, "prefill512.hip": _PROMPT}
+EXTRA = {"prefill.hip": _PROMPT, "prefill512.hip": _PROMPT, "decode.hip": _PROMPT}
 NOISE = "is not a recognized feature for this target"
 
 

@@ -99,6 +99,52 @@ int attn_decode(void* out, const void* q, const void* k_cache,
     return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
+size_t attn_decode_rows_workspace_bytes(int n_seq, int rows, int n_q_heads, int head_dim,
+                                        int cache_cap) {
+    if (rows < 1 || rows > ATTN_DECODE_MAX_ROWS || n_seq < 0 ||
+        (long long)n_seq * rows > 0x7FFFFFFFLL)
+        return 0;
+    return attn_decode_workspace_bytes(n_seq * rows, n_q_heads, head_dim, cache_cap);
+}
+
+int attn_decode_rows(void* out, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* pos, int n_seq, int rows,
+                     int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
+                     int ring, int window, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+    if (st != ATTN_OK) return st;
+    if (n_seq < 0 || rows < 1 || rows > ATTN_DECODE_MAX_ROWS || (ring != 0 && ring != 1) ||
+        !isfinite(scale))
+        return ATTN_E_RANGE;
+    if (cache_cap < 1) return ATTN_E_CACHE;
+    if (window < 0) return ATTN_E_WINDOW;
+    if (ring && (window < 1 || (long long)window + rows - 1 > cache_cap)) return ATTN_E_WINDOW;
+    if (tensor_bytes(n_seq, n_kv_heads, cache_cap, head_dim) < 0 ||
+        tensor_bytes((long long)n_seq * rows, n_q_heads, 1, head_dim) < 0)
+        return ATTN_E_RANGE;
+    if (n_seq == 0) return ATTN_OK;
+    if (!out || !q || !k_cache || !v_cache || !pos) return ATTN_E_NULL;
+    if (!workspace) return ATTN_E_WORKSPACE;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(pos) & 3u) != 0)
+        return ATTN_E_ALIGN;
+    const size_t need =
+        attn_decode_rows_workspace_bytes(n_seq, rows, n_q_heads, head_dim, cache_cap);
+    if (need == 0) return ATTN_E_RANGE;
+    if (workspace_bytes < need) return ATTN_E_WORKSPACE;
+    if (n_seq > 65535 || n_kv_heads > 65535 ||
+        (cache_cap + ATTN_DECODE_CHUNK - 1) / ATTN_DECODE_CHUNK > 0x7FFFFFFF / 2)
+        return ATTN_E_RANGE;
+    hipError_t e = launch_decode_rows(
+        static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+        static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+        pos, n_seq, rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring, window,
+        scale, workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
 int attn_prefill_key_block(int head_dim, int p_mode) {
     if (head_dim != 256 && head_dim != 512) return ATTN_E_HEAD_DIM;
     if (p_mode != ATTN_P_BF16 && p_mode != ATTN_P_BF16X2) return ATTN_E_P_MODE;

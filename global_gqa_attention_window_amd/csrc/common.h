@@ -107,6 +107,39 @@ ATTN_DEV void dma16_asm_sbase(const void* base, uint32_t voff, uint32_t lds_byte
 #endif
 }
 
+// Element offset of row r of a K or V block staged in LDS.  D = 512: rows of
+// 1 KiB, each followed by PADP padding elements.  D = 256: rows r and r + 8
+// of each 16-row group share one 1 KiB unit (the two halves of a DMA
+// instruction's 64 lanes), units followed by PADP padding elements.
+template <int D, int PADP>
+ATTN_DEV constexpr int row_pos(int r) {
+    if constexpr (D == 512) {
+        return r * (D + PADP);
+    } else {
+        return ((r >> 4) * 8 + (r & 7)) * (2 * D + PADP) + ((r >> 3) & 1) * D;
+    }
+}
+
+// Whether a cache slot is attended by a decode row at position t, and the
+// position it holds: a linear cache holds position `slot`; a ring of cap
+// slots the latest position p <= t with p = slot (mod cap).  Attended: 0 <=
+// p <= t and, with a window W > 0, t - p < W.  Slots at or past cap, and
+// rows at t < 0, attend nothing.
+ATTN_DEV bool slot_attended(int slot, int t, int cap, int ring, int window) {
+    if (slot >= cap || t < 0) return false;
+    int p;
+    if (ring) {
+        int d = (t - slot) % cap;
+        if (d < 0) d += cap;
+        p = t - d;
+    } else {
+        p = slot;
+    }
+    if (p < 0 || p > t) return false;
+    if (window > 0 && t - p >= window) return false;
+    return true;
+}
+
 // LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lane j points at four consecutive 16-bit elements M[j][0..3]; lane i gets
 // back M[4 k + (i >> 2)][i & 3] for k = 0..3 (measured on gfx950).  Pointing

@@ -1,288 +1,346 @@
-// Decode attention on gfx950: 256-slot chunk partials, merged in chunk order.
+// Decode attention on gfx950: chunk partials over the KV cache, merged in
+// chunk order, for one row or a window of up to 16 consecutive rows per
+// stream.
 //
 // Method: TensorFold PR #1183 "cuda gemma4: images on the 12B ...", squashed
 // commit bodies (window_rows notes): a head's keys split into 256-key chunks,
-// each leaving a partial (max, sum, accumulator), merged in chunk order; at
-// head dim 512 a block serves several query heads and a warp a run of keys.
+// each leaving a partial (max, sum, accumulator), merged in chunk order.
 // PR #975 "Gemma 4 12B on the native Metal engine", decode attention commits:
-// a KV head's query heads form one 16-row tile so every key and value is read
-// once per token; chunks spread over workgroups and leave partials for a merge.
-//
-// MI355X design.  One wave64 per (stream, KV head, chunk).  The 16 rows of
-// the matrix-core tile are the G <= 16 query heads of the KV head (rows past
-// G hold zero queries and are never stored).  The wave walks its chunk in
-// 16-key tiles with an online softmax:
-//   S^T[key][head] = K . Q^T   on v_mfma_f32_16x16x32_bf16; each lane loads
-//                               16 contiguous bytes of a K row straight from
-//                               HBM (four lanes cover 64 contiguous bytes of
-//                               one row per load), Q^T sits in registers;
-//   O^T[d][head] += V^T . P^T  on v_mfma_f32_16x16x4_f32 with p in fp32, so
-//                               p is never rounded; each lane loads 16 bytes
-//                               of a V row (sixteen lanes cover 256 contiguous
-//                               bytes), widening bf16 to fp32 in registers.
-// With S^T as the score layout, lane l always owns query head l % 16: its row
-// maximum, rescale factor and accumulator stay in the lane, and only the four
-// lanes of one head (l, l^16, l^32, l^48) exchange maxima and sums.
-// Keys that are not attended (outside the window, beyond the row, never
-// written, past the cache end) get p = 0 and their V values are replaced by
-// zeros before the products, so NaN in such slots cannot reach the output.
+// a KV head's query heads (and several decode rows) form one 16-row tile so
+// every key and value is read once per window; chunks spread over
+// workgroups and leave partials for a merge; every row keeps its bits at any
+// window width.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
-constexpr int CHUNK = 256;
-constexpr int TILE = 16;
+constexpr int CHUNK = ATTN_DECODE_CHUNK;
 
-// position held by `slot` for a row at position t, and whether it is attended
-ATTN_DEV bool slot_attended(int slot, int t, int cap, int ring, int window) {
-    if (slot >= cap || t < 0) return false;
-    int p;
-    if (ring) {
-        int d = (t - slot) % cap;
-        if (d < 0) d += cap;
-        p = t - d;
-    } else {
-        p = slot;
-    }
-    if (p < 0 || p > t) return false;
-    if (window > 0 && t - p >= window) return false;
-    return true;
+// Decode windows: R <= 16 rows per stream, row r at position pos[s] + r
+// (PR #975 decode attention commits: a key head's query heads and two decode
+// rows fill one 16-row tile, so each key and value is read once for the
+// window; PR #1183 engine note: windows of up to 16 rows a stream).
+//
+// A matrix-core column is one (row, query head) pair: a 16-column tile holds
+// RPT = 16 / G rows of the G query heads of a KV head.  A workgroup of four
+// waves takes 4 / DS column tiles of one (stream, KV head, run of chunks);
+// the DS waves of a tile split its output d range (all of them form the
+// tile's scores, so a column's arithmetic is the same for every DS).  32-key
+// blocks of K and V are staged in LDS by direct global->LDS loads, two
+// stages shared by the four waves.  Per block and column:
+//   S^T = K . Q^T               bf16 products, two 16-key tiles;
+//   reference maximum           as in the one-row kernel (moves only when the
+//                               block maximum passes it by 8), so p <= 2^8;
+//   p = exp2(s c - m), fp32     never rounded: p = hi + mid + lo exactly,
+//                               hi = bf16(p), mid = bf16(p - hi), lo =
+//                               bf16(p - hi - mid) (24 significant bits in
+//                               three 8-bit pieces), and
+//   O^T += V^T . {hi, mid, lo}  three bf16 products per d tile, fp32
+//                               accumulation: fp32 probabilities on the bf16
+//                               matrix cores, at 3/16 of the fp32 path's
+//                               matrix time.
+// V^T comes from the staged rows by transpose reads.  A key no row of the
+// workgroup attends is fetched from the slot of the window's last row
+// instead (masked, finite: it adds exactly zero); a key some rows attend and
+// others do not has p = 0 in the others.  Each (row, head) leaves one
+// partial per run, merged by decode_merge_kernel.  The arithmetic of a
+// column depends neither on the other columns of its tile nor on R, so a
+// row keeps its bits at any window width.
+constexpr int WKB = 32;        // keys per block (one P.V product)
+
+// Chunks per run: a workgroup carries one online softmax over a run of
+// consecutive chunks and leaves one partial for it.  Runs grow with the cache
+// (fewer partials to write and merge) up to four chunks; the length depends
+// on the cache capacity alone, so a row's bits depend neither on the number
+// of streams nor on the window width.
+int decode_run_chunks(int cap) {
+    const int nch = (cap + CHUNK - 1) / CHUNK;
+    const int r = nch / 32;
+    return r < 1 ? 1 : (r > 4 ? 4 : r);
 }
+constexpr int WPAD = 16;       // LDS padding elements per row (per row pair at 256)
 
-template <int D>
-__global__ __launch_bounds__(64)
-void decode_partial_kernel(const uint16_t* __restrict__ q,
-                           const uint16_t* __restrict__ kc,
-                           const uint16_t* __restrict__ vc,
-                           const int32_t* __restrict__ pos,
-                           float* __restrict__ part_acc,
-                           float* __restrict__ part_ml,
-                           int Hq, int Hkv, int G, int cap, int nrun, int cpr,
-                           int ring, int window, float c) {
-    constexpr int QST = D / 32;       // 32-wide reduction steps of Q.K
-    constexpr int SPANS = D / 128;    // 128-wide d spans of the accumulator
-    constexpr int LPR = D / 8;        // lanes that move one K row per DMA
-    constexpr int RPD = 64 / LPR;     // K rows per DMA instruction
-    const int run = blockIdx.x;
-    const int g = blockIdx.y;
-    const int s = blockIdx.z;
-    const int lane = threadIdx.x;
+template <int D, int DS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_rows_kernel(const uint16_t* __restrict__ q,
+                        const uint16_t* __restrict__ kc,
+                        const uint16_t* __restrict__ vc,
+                        const int32_t* __restrict__ pos,
+                        float* __restrict__ part_acc,
+                        float* __restrict__ part_ml,
+                        int R, int Hq, int Hkv, int G, int RPT, int NT, int CG,
+                        int n_items, int cap, int nrun, int cpr, int ring, int window,
+                        float c) {
+    constexpr int WC = 4 / DS;                  // column tiles per workgroup
+    constexpr int QST = D / 32;                 // reduction steps of a score
+    constexpr int DTW = D / 16 / DS;            // 16-wide d tiles of this wave
+    constexpr int LPR = D / 8;                  // lanes moving one row per DMA
+    constexpr int NI = WKB * LPR / 64;          // DMA instructions per K (or V) block
+    constexpr int NIW = NI / 4;                 // ... issued by each wave
+    constexpr int BLK = row_pos<D, WPAD>(WKB);
+    constexpr int K16 = row_pos<D, WPAD>(16);   // rows 16.. of a block
+    constexpr int KPF = 4;                      // score steps of K reads in flight
+    constexpr int VG = DTW < 4 ? DTW : 4;       // d tiles per P.V group
+    constexpr int NG = DTW / VG;                // P.V groups
+    static_assert(NIW * 4 == NI && NG * VG == DTW && QST >= KPF && (2 * NIW) % QST == 0,
+                  "shapes");
+
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2][BLK];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[2][BLK];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int col = lane & 15;
     const int grp = lane >> 4;
-    const int t = pos[s];
 
-    // K tiles land here by direct global->LDS loads, two stages
-    __shared__ __attribute__((aligned(16))) uint16_t ks[2][TILE * D];
+    // the CG workgroups of item u are consecutive on one XCD (the hardware
+    // deals workgroup L to XCD L % 8), so its K/V blocks come from HBM once
+    const int L = blockIdx.x;
+    const int cgi = (L >> 3) % CG;
+    const int u = ((L >> 3) / CG) * 8 + (L & 7);
+    if (u >= n_items) return;
+    const int run = u % nrun;
+    const int g = (u / nrun) % Hkv;
+    const int s = u / (nrun * Hkv);
 
-    const size_t head_base = ((size_t)s * Hkv + g) * (size_t)cap;
-    const uint16_t* K = kc + head_base * D;
-    const uint16_t* V = vc + head_base * D;
-    const int h0 = g * G;
-    const size_t pbase = ((size_t)s * Hq + h0) * (size_t)nrun + run;
+    // this wave: column tile ct (RPT rows x G heads), d part dp
+    const int ct = cgi * WC + wave / DS;
+    const int dp = wave % DS;
+    const int rr = ct * RPT + col / G;
+    const int h = g * G + col % G;
+    const bool cv = ct < NT && col < RPT * G && rr < R;
+    const int p0 = pos[s];
+    const int t_col = cv ? p0 + rr : -1;
+    // the workgroup's rows t0..t1: a slot one of them attends is one the last
+    // row attends under a window widened by t1 - t0
+    const int r_lo = cgi * WC * RPT;
+    const int r_hi = min(R, (cgi + 1) * WC * RPT) - 1;
+    const int t1 = p0 + r_hi;
+    const int t0 = max(p0 + r_lo, 0);
+    const int w_all = window > 0 ? window + (t1 - t0) : 0;
+    const size_t pidx = (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * (size_t)nrun + run;
+    // t mod cap, taken once: a ring slot's position for a row at t is then
+    // t - ((t mod cap) - slot, plus cap when negative), with no division
+    const int t1m = t1 >= 0 ? t1 % cap : 0;
+    const int tcm = t_col >= 0 ? t_col % cap : 0;
+    // slot attended by a row at t (tm = t mod cap) under window w; written
+    // with selects only, so the callers' instruction order is never cut by
+    // branches
+    auto attended = [&](int slot, int t, int tm, int w) -> bool {
+        int d = tm - slot;
+        d += d < 0 ? cap : 0;
+        const int p = ring ? t - d : slot;
+        return (slot < cap) & (t >= 0) & (p >= 0) & (p <= t) & ((w <= 0) | (t - p < w));
+    };
+
     const int slot0 = run * cpr * CHUNK;
     const int nslot = min(cpr * CHUNK, cap - slot0);
-    const int ntile = (nslot + TILE - 1) / TILE;
-
-    // attended tiles of this run: [tt_lo, tt_hi]; a run with none writes an
-    // empty partial (m = -inf, l = 0) that the merge skips
-    int tt_lo = 0x7FFFFFFF, tt_hi = -1;
-    for (int tb = 0; tb < ntile; tb += 16) {
+    const int nblk = (nslot + WKB - 1) / WKB;
+    int bb_lo = 0x7FFFFFFF, bb_hi = -1;
+    for (int b0 = 0; b0 < nblk; b0 += 8) {
+        const int bb = b0 + (lane >> 3);         // lane covers 4 slots of block bb
         bool mine = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            mine |= slot_attended(slot0 + (tb + lane / 4) * TILE + 4 * (lane & 3) + i, t, cap, ring, window);
-        const uint64_t bal = __ballot(mine);     // lane covers tile tb + lane / 4
+            mine |= (bb < nblk) & attended(slot0 + bb * WKB + 4 * (lane & 7) + i, t1, t1m, w_all);
+        const uint64_t bal = __ballot(mine);
         if (bal != 0) {
-            tt_lo = min(tt_lo, tb + __builtin_ctzll(bal) / 4);
-            tt_hi = tb + (63 - __builtin_clzll(bal)) / 4;
+            bb_lo = min(bb_lo, b0 + __builtin_ctzll(bal) / 8);
+            bb_hi = b0 + (63 - __builtin_clzll(bal)) / 8;
         }
     }
-    if (tt_hi < 0) {
-        if (col < G && grp == 0) {
-            part_ml[2 * (pbase + (size_t)col * nrun) + 0] = -INFINITY;
-            part_ml[2 * (pbase + (size_t)col * nrun) + 1] = 0.f;
+    if (bb_hi < 0) {
+        if (cv && dp == 0 && grp == 0) {
+            part_ml[2 * pidx + 0] = -INFINITY;
+            part_ml[2 * pidx + 1] = 0.f;
         }
         return;
     }
 
-    // Q^T operand: lane holds Q[head col][32 st + 8 grp .. +7]
+    // Q^T operand in AGPRs: Q[column][32 st + 8 grp .. +7]
     u32x4 qreg[QST];
     {
-        const bool hv = col < G;
-        const uint16_t* qrow = q + ((size_t)s * Hq + h0 + (hv ? col : 0)) * D;
+        const uint16_t* qrow = q + (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * D + 8 * grp;
 #pragma unroll
         for (int st = 0; st < QST; ++st) {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            qreg[st] = hv ? ld16(qrow + 32 * st + 8 * grp) : z;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qreg[st] = cv ? ld16(qrow + 32 * st) : z;
         }
-        // Q lives in AGPRs (the score products read their B operand there),
-        // leaving the VGPRs to the accumulator and two tiles of V
 #pragma unroll
         for (int st = 0; st < QST; ++st) asm volatile("" : "+a"(qreg[st]));
     }
 
-    f32x4 acc[SPANS][8];
-#pragma unroll
-    for (int sp = 0; sp < SPANS; ++sp)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[sp][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const size_t head_base = ((size_t)s * Hkv + g) * (size_t)cap * D;
+    const uint16_t* Kh = kc + head_base;
+    const uint16_t* Vh = vc + head_base;
+    const int sub = ring ? t1 % cap : min(t1, cap - 1);     // t1 >= 0 here
 
-    // K tile: each DMA instruction moves 1 KiB of whole rows (one row at
-    // D=512, two at 256).  16-byte chunk c of row r sits at chunk c ^ (r & 7)
-    // of its LDS row, so the eight lanes of one LDS read phase (eight rows,
-    // same chunk) hit eight different bank groups.  The slot is clamped in
-    // range; a key that is not attended is masked out of the scores.
-    // (issued from asm, one instruction at a time between the score
-    // products: the compiler then adds no wait for it before the LDS reads
-    // of the other stage; the tile loop waits for it explicitly)
-    auto load_k_one = [&](int sb, int stage, int i) {
-        const int row = i * RPD + lane / LPR;
-        const int slot = min(sb + row, cap - 1);
-        const int chunk = (lane % LPR) ^ (row & 7);
-        dma16_asm(K + (size_t)slot * D + chunk * 8, lds_addr(&ks[stage][i * RPD * D]));
-    };
-    auto load_k = [&](int sb, int stage) {
+    // DMA instruction i = wave + 4 k of a K or V block moves 1 KiB: block row
+    // i at D = 512, rows 16 (i >> 3) + (i & 7) and + 8 at D = 256 (lanes
+    // 0..31, 32..63).  The lane's source row and LDS offset per k are fixed.
+    int dma_row[NIW];
+    int dma_dst[NIW];
 #pragma unroll
-        for (int i = 0; i < TILE / RPD; ++i) load_k_one(sb, stage, i);
-    };
-    // V rows (sb + 4 grp + r), d = 128 sp + 8 col .. +7: sixteen lanes read
-    // 256 contiguous bytes of one row per load
-    u32x4 vbuf0[4][SPANS];
-    u32x4 vbuf1[4][SPANS];
-    auto load_v = [&](int sb, u32x4 (&dst)[4][SPANS]) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int slot = min(sb + 4 * grp + r, cap - 1);
-            const uint16_t* vrow = V + (size_t)slot * D + 8 * col;
-#pragma unroll
-            for (int sp = 0; sp < SPANS; ++sp) dst[r][sp] = ld16(vrow + 128 * sp);
-        }
+    for (int k = 0; k < NIW; ++k) {
+        const int i = wave + 4 * k;
+        const int r0 = (LPR == 64) ? i : 16 * (i >> 3) + (i & 7);
+        dma_row[k] = (LPR == 64) ? r0 : r0 + 8 * (lane >> 5);
+        dma_dst[k] = row_pos<D, WPAD>(r0);
+    }
+    auto dma_one = [&](const uint16_t* base, uint16_t* stage, int b, int k) {
+        int slot = slot0 + b * WKB + dma_row[k];
+        slot = attended(slot, t1, t1m, w_all) ? slot : sub;
+        dma16_asm(base + (size_t)slot * D + (lane % LPR) * 8, lds_addr(stage + dma_dst[k]));
     };
 
+    f32x4 acc[DTW];
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    // One 16-key tile; V of this tile in vc, the next tile's V goes to vn.
-    static_assert(TILE / RPD == QST, "one K DMA instruction per score product");
-    auto tile = [&](int tt, const u32x4 (&vc)[4][SPANS], u32x4 (&vn)[4][SPANS]) {
-        const int stage = (tt - tt_lo) & 1;
-        const int sb = slot0 + tt * TILE;
-        const bool more = tt < tt_hi;
-        // K(tt) in LDS and V(tt) in registers have landed
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (more) load_v(sb + TILE, vn);         // in flight through this tile
+    const int kofs = row_pos<D, WPAD>(col) + 8 * grp;
+    // V^T operand: lane j of a 16-lane group points at the row of k-slot
+    // j >> 2 (keys 4 grp + (col >> 2), and + 16), columns 16 dt + 4 (j & 3)
+    // of the wave's d part
+    const int vofs = row_pos<D, WPAD>(4 * grp + (col >> 2)) + 4 * (col & 3) + dp * (D / DS);
 
-        // scores: the two halves of the head dim accumulate separately (two
-        // independent product chains) and are added at the end; the next
-        // tile's K moves in beside them, one DMA instruction per product
-        const uint16_t* kt = &ks[stage][0];
-        f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb2 = {0.f, 0.f, 0.f, 0.f};
+    // One block from stage st; with MORE, the next block's K and V move into
+    // the other stage beside the score products.
+    auto block = [&](int b, int st, auto more_c) {
+        constexpr bool MORE = decltype(more_c)::value;
+        const uint16_t* kl = ks[st];
+        const uint16_t* vl = vs[st];
+
+        u32x4 kb[KPF][2];
 #pragma unroll
-        for (int st = 0; st < QST; ++st) {
-            const u32x4 kop = ld16(kt + col * D + 8 * ((4 * st + grp) ^ (col & 7)));
-            if (st < QST / 2) sa = mfma_bf16_16x16x32(kop, qreg[st], sa);
-            else sb2 = mfma_bf16_16x16x32(kop, qreg[st], sb2);
-            if (more) load_k_one(sb + TILE, stage ^ 1, st);
+        for (int j = 0; j < KPF; ++j) {
+            kb[j][0] = ld16(kl + kofs + 32 * j);
+            kb[j][1] = ld16(kl + K16 + kofs + 32 * j);
         }
-        const f32x4 sc = sa + sb2;
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        // each step: two products, the reads KPF steps ahead, the step's
+        // share of the DMA; fenced so the reads stay ahead of their use
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < QST; ++j) {
+            s0 = mfma_bf16_16x16x32(kb[j % KPF][0], qreg[j], s0);
+            s1 = mfma_bf16_16x16x32(kb[j % KPF][1], qreg[j], s1);
+            if (j + KPF < QST) {
+                kb[j % KPF][0] = ld16(kl + kofs + 32 * (j + KPF));
+                kb[j % KPF][1] = ld16(kl + K16 + kofs + 32 * (j + KPF));
+            }
+            if constexpr (MORE) {
+                // both stages of the next block go out during the scores, so
+                // they have the whole block to land
+#pragma unroll
+                for (int k = j * 2 * NIW / QST; k < (j + 1) * 2 * NIW / QST; ++k) {
+                    if (k < NIW) dma_one(Kh, ks[st ^ 1], b + 1, k);
+                    else dma_one(Vh, vs[st ^ 1], b + 1, k - NIW);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // first V^T group's reads go out before the softmax
+        u32x4 va[2][VG];
+        auto rd_v = [&](int dt) -> u32x4 {
+            const u32x2 x0 = lds_read_tr16(vl + vofs + 16 * dt);
+            const u32x2 x1 = lds_read_tr16(vl + K16 + vofs + 16 * dt);
+            return u32x4{x0.x, x0.y, x1.x, x1.y};
+        };
+#pragma unroll
+        for (int e = 0; e < VG; ++e) va[0][e] = rd_v(e);
 
-        float tv[4];
-        uint32_t vmask[4], vsel[4];
+        const int sb = slot0 + b * WKB;
+        float tv[8];
         float mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool ok = slot_attended(sb + 4 * grp + i, t, cap, ring, window);
-            tv[i] = ok ? sc[i] * c : -INFINITY;
-            mx = fmaxf(mx, tv[i]);
-            // bf16 -> fp32 of V with unattended keys forced to +0 (a NaN
-            // there must not meet its zero probability)
-            vmask[i] = ok ? 0xFFFF0000u : 0u;
-            vsel[i] = ok ? 0x01000C0Cu : 0x0C0C0C0Cu;
+            const bool ok0 = attended(sb + 4 * grp + i, t_col, tcm, window);
+            const bool ok1 = attended(sb + 16 + 4 * grp + i, t_col, tcm, window);
+            tv[i] = ok0 ? s0[i] * c : -INFINITY;
+            tv[4 + i] = ok1 ? s1[i] * c : -INFINITY;
+            mx = fmaxf(mx, fmaxf(tv[i], tv[4 + i]));
         }
-        // Reference maximum.  Decode keeps p in fp32 and never rounds it
-        // against the maximum, so the maximum only keeps exp2 in range: it
-        // moves (and the accumulator is rescaled) only when a tile's maximum
-        // passes it by more than 8, so p <= 2^8 and a run's row sum stays
-        // below 2^18, far inside fp32; the partial carries the reference it
-        // used, which the merge takes as the chunk maximum.
+        // reference maximum: moves only when the block maximum passes it by
+        // more than 8 (p <= 2^8); a lane that keeps it keeps its bits
         mx = xmax4(mx);
-        const bool grow = mx > m_run + 8.f;       // first attended tile: m_run = -inf
+        const bool grow = mx > m_run + 8.f;
         if (__any(grow)) {
             const float m_new = grow ? mx : m_run;
-            // 0 when growing from -inf; exactly 1 for a lane that keeps its
-            // reference (also one still at -inf, where the difference is NaN)
             const float alpha = grow ? fast_exp2(m_run - mx) : 1.f;
             l_run *= alpha;
 #pragma unroll
-            for (int sp = 0; sp < SPANS; ++sp)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[sp][j] *= alpha;
+            for (int dt = 0; dt < DTW; ++dt) acc[dt] *= alpha;
             m_run = m_new;
         }
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float pv[4];
         float psum = 0.f;
+        uint32_t ph[4], pm[4], pl[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pv[i] = fast_exp2(tv[i] - m_use);              // 0 for masked keys
-            psum += pv[i];
+        for (int k = 0; k < 4; ++k) {
+            // B operand slots 2 k, 2 k + 1: slots 0..3 are keys 4 grp + i of
+            // tile 0, slots 4..7 those of tile 1
+            const float pa = fast_exp2(tv[2 * k] - m_use);
+            const float pb = fast_exp2(tv[2 * k + 1] - m_use);
+            psum += pa + pb;
+            ph[k] = cvt_pk_bf16(pa, pb);
+            const float ra = pa - bf16lo_to_f32(ph[k]);
+            const float rb = pb - bf16hi_to_f32(ph[k]);
+            pm[k] = cvt_pk_bf16(ra, rb);
+            pl[k] = cvt_pk_bf16(ra - bf16lo_to_f32(pm[k]), rb - bf16hi_to_f32(pm[k]));
         }
         l_run += psum;
+        const u32x4 bp[3] = {{ph[0], ph[1], ph[2], ph[3]}, {pm[0], pm[1], pm[2], pm[3]},
+                             {pl[0], pl[1], pl[2], pl[3]}};
+
+        // O^T += V^T . P^T in groups of VG d tiles: the group's products go
+        // hi, mid, lo across its tiles (each accumulator's next product is VG
+        // products later), the next group's reads beside them
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int gi = 0; gi < NG; ++gi) {
+            if (gi + 1 < NG) {
 #pragma unroll
-            for (int sp = 0; sp < SPANS; ++sp) {
-                const u32x4 w = vc[r][sp];
-                const float p = pv[r];
-                const uint32_t sl = vsel[r], mk = vmask[r];
-#define LO(x) __uint_as_float(__builtin_amdgcn_perm(0u, (x), sl))
-#define HI(x) __uint_as_float((x) & mk)
-                acc[sp][0] = mfma_f32_16x16x4(LO(w.x), p, acc[sp][0]);
-                acc[sp][1] = mfma_f32_16x16x4(HI(w.x), p, acc[sp][1]);
-                acc[sp][2] = mfma_f32_16x16x4(LO(w.y), p, acc[sp][2]);
-                acc[sp][3] = mfma_f32_16x16x4(HI(w.y), p, acc[sp][3]);
-                acc[sp][4] = mfma_f32_16x16x4(LO(w.z), p, acc[sp][4]);
-                acc[sp][5] = mfma_f32_16x16x4(HI(w.z), p, acc[sp][5]);
-                acc[sp][6] = mfma_f32_16x16x4(LO(w.w), p, acc[sp][6]);
-                acc[sp][7] = mfma_f32_16x16x4(HI(w.w), p, acc[sp][7]);
-#undef LO
-#undef HI
+                for (int e = 0; e < VG; ++e) va[(gi + 1) & 1][e] = rd_v((gi + 1) * VG + e);
             }
+#pragma unroll
+            for (int x = 0; x < 3; ++x)
+#pragma unroll
+                for (int e = 0; e < VG; ++e)
+                    acc[gi * VG + e] = mfma_bf16_16x16x32(va[gi & 1][e], bp[x], acc[gi * VG + e]);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    load_k(slot0 + tt_lo * TILE, 0);
-    load_v(slot0 + tt_lo * TILE, vbuf0);
-    for (int tt = tt_lo; tt <= tt_hi; ++tt) {
-        tile(tt, vbuf0, vbuf1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int sp = 0; sp < SPANS; ++sp) vbuf0[r][sp] = vbuf1[r][sp];
+    for (int k = 0; k < NIW; ++k) {
+        dma_one(Kh, ks[0], bb_lo, k);
+        dma_one(Vh, vs[0], bb_lo, k);
+    }
+    for (int b = bb_lo; b <= bb_hi; ++b) {
+        // block b has landed (every wave's share), and every wave is done
+        // with block b - 1's stage
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (b < bb_hi) block(b, (b - bb_lo) & 1, std::true_type{});
+        else block(b, (b - bb_lo) & 1, std::false_type{});
     }
 
     const float l_tot = xsum4(l_run);
-    if (col >= G) return;
-    const size_t pidx = pbase + (size_t)col * nrun;
-    if (grp == 0) {
+    if (!cv) return;
+    if (dp == 0 && grp == 0) {
         part_ml[2 * pidx + 0] = m_run;
         part_ml[2 * pidx + 1] = l_tot;
     }
-    float* dst = part_acc + pidx * D;
-    // lane holds d = 128 sp + 32 grp + 8 i + j in acc[sp][j][i]
+    // lane holds d = dp D / DS + 16 dt + 4 grp + i of its column in acc[dt][i]
+    float* dst = part_acc + pidx * D + dp * (D / DS) + 4 * grp;
 #pragma unroll
-    for (int sp = 0; sp < SPANS; ++sp) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float* p = dst + 128 * sp + 32 * grp + 8 * i;
-            f32x4 lo = {acc[sp][0][i], acc[sp][1][i], acc[sp][2][i], acc[sp][3][i]};
-            f32x4 hi = {acc[sp][4][i], acc[sp][5][i], acc[sp][6][i], acc[sp][7][i]};
-            *reinterpret_cast<f32x4*>(p) = lo;
-            *reinterpret_cast<f32x4*>(p + 4) = hi;
-        }
-    }
+    for (int dt = 0; dt < DTW; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = acc[dt];
 }
 
 // Merge of chunk partials in ascending chunk order.  A block of MW waves
@@ -378,26 +436,57 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                          const uint16_t* vc, const int32_t* pos, int S, int Hq,
                          int Hkv, int D, int cap, int ring, int window,
                          float scale, void* ws, hipStream_t stream) {
-    const int nch = (cap + CHUNK - 1) / CHUNK;
-    // a workgroup carries its softmax over a run of consecutive chunks; runs
-    // of two when there are chunks for more than one wave per SIMD
-    const long long waves = (long long)nch * Hkv * S;
-    const int cpr = waves > 1536 ? 2 : 1;
-    const int nrun = (nch + cpr - 1) / cpr;
-    const int G = Hq / Hkv;
-    float* part_acc = reinterpret_cast<float*>(ws);
-    float* part_ml = part_acc + (size_t)S * Hq * nrun * D;
-    const float c = scale * ATTN_LOG2E;
-    dim3 g1(nrun, Hkv, S);
-    dim3 g2(S * Hq, D / 256);
-    if (D == 256) {
-        decode_partial_kernel<256><<<g1, 64, 0, stream>>>(q, kc, vc, pos, part_acc, part_ml,
-                                                          Hq, Hkv, G, cap, nrun, cpr, ring, window, c);
-        decode_merge_kernel<256><<<g2, 64 * MW, 0, stream>>>(out, part_acc, part_ml, Hq, nrun);
-    } else {
-        decode_partial_kernel<512><<<g1, 64, 0, stream>>>(q, kc, vc, pos, part_acc, part_ml,
-                                                          Hq, Hkv, G, cap, nrun, cpr, ring, window, c);
-        decode_merge_kernel<512><<<g2, 64 * MW, 0, stream>>>(out, part_acc, part_ml, Hq, nrun);
-    }
+    // one row per stream is a window of one row: the same kernel and bits
+    return launch_decode_rows(out, q, kc, vc, pos, S, 1, Hq, Hkv, D, cap, ring, window, scale,
+                              ws, stream);
+}
+
+static hipError_t launch_decode_merge(uint16_t* out, const float* part_acc, const float* part_ml,
+                               int n_rows_heads, int D, int nrun, hipStream_t stream) {
+    const dim3 g2(n_rows_heads, D / 256);
+    if (D == 256)
+        decode_merge_kernel<256><<<g2, 64 * MW, 0, stream>>>(out, part_acc, part_ml, 0, nrun);
+    else
+        decode_merge_kernel<512><<<g2, 64 * MW, 0, stream>>>(out, part_acc, part_ml, 0, nrun);
     return hipGetLastError();
+}
+
+hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* kc,
+                              const uint16_t* vc, const int32_t* pos, int S, int R, int Hq,
+                              int Hkv, int D, int cap, int ring, int window, float scale,
+                              void* ws, hipStream_t stream) {
+    const int G = Hq / Hkv;
+    const int RPT = 16 / G;                      // rows per 16-column tile
+    const int NT = (R + RPT - 1) / RPT;          // column tiles of a window
+    // four waves a workgroup: one tile split four ways over d, two tiles two
+    // ways, or four tiles (three leave one wave idle)
+    const int DS = NT == 1 ? 4 : (NT == 2 ? 2 : 1);
+    const int WC = 4 / DS;
+    const int CG = (NT + WC - 1) / WC;           // workgroups per item
+    const int nch = (cap + CHUNK - 1) / CHUNK;
+    const int cpr = decode_run_chunks(cap);
+    const int nrun = (nch + cpr - 1) / cpr;
+    const long long n_items = (long long)nrun * Hkv * S;
+    const long long nwg = (n_items + 7) / 8 * 8 * CG;
+    if (nwg > 0x7FFFFFFFLL || (long long)S * R * Hq > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+    float* part_acc = reinterpret_cast<float*>(ws);
+    float* part_ml = part_acc + (size_t)S * R * Hq * nrun * D;
+    const float c = scale * ATTN_LOG2E;
+#define ROWS_LAUNCH(DD, SS)                                                                   \
+    decode_rows_kernel<DD, SS><<<(unsigned)nwg, 256, 0, stream>>>(                            \
+        q, kc, vc, pos, part_acc, part_ml, R, Hq, Hkv, G, RPT, NT, CG, (int)n_items, cap,     \
+        nrun, cpr, ring, window, c)
+    if (D == 256) {
+        if (DS == 4) ROWS_LAUNCH(256, 4);
+        else if (DS == 2) ROWS_LAUNCH(256, 2);
+        else ROWS_LAUNCH(256, 1);
+    } else {
+        if (DS == 4) ROWS_LAUNCH(512, 4);
+        else if (DS == 2) ROWS_LAUNCH(512, 2);
+        else ROWS_LAUNCH(512, 1);
+    }
+#undef ROWS_LAUNCH
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_decode_merge(out, part_acc, part_ml, S * R * Hq, D, nrun, stream);
 }

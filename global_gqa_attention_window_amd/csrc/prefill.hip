@@ -49,15 +49,6 @@ template <int D> struct PrefillCfg;
 template <> struct PrefillCfg<256> { static constexpr int KB = 64; };
 template <> struct PrefillCfg<512> { static constexpr int KB = 32; };
 
-// element offset of block row r in LDS (PADP: padding elements per unit)
-template <int D, int PADP>
-ATTN_DEV constexpr int row_pos(int r) {
-    if constexpr (D == 512) {
-        return r * (D + PADP);
-    } else {
-        return ((r >> 4) * 8 + (r & 7)) * (2 * D + PADP) + ((r >> 3) & 1) * D;
-    }
-}
 
 // Operations per stage of the staged softmax (see the kernel) for NE
 // probabilities per lane, and the P.V steps its plan takes at cap

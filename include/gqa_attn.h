@@ -95,12 +95,16 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_q_heads, int head_dim,
  * One decode row per stream (PR #1183 window_rows notes; PR #975 decode
  * attention commits).  For stream s and query head h, with t = pos[s]:
  * keys are the cache slots whose position is attended by a row at t; each
- * 256-slot chunk c yields m_c = max score, l_c = sum exp(s - m_c) and
- * acc_c = sum exp(s - m_c) v; chunks merge in ascending order over the
- * largest m_c; out = bf16(sum e^(m_c - M) acc_c / sum e^(m_c - M) l_c).
- * Scores are scale * q.k with fp32 accumulation; probabilities are not
- * rounded to bf16 (carried to 16 significant bits for the matrix cores).
- * A row with no attended key (t < 0) gives +0.
+ * run c of consecutive 256-slot chunks (1 to 4 chunks, fixed by cap alone)
+ * yields m_c (a reference maximum within 8 of the run's largest score, in
+ * log2 units), l_c = sum 2^(s log2(e) - m_c) and acc_c = the same weights
+ * times v; runs merge in ascending order over M = max m_c; out =
+ * bf16(sum e^(m_c - M) acc_c / sum e^(m_c - M) l_c).  Scores are scale * q.k
+ * with fp32 accumulation; probabilities stay fp32, never rounded to bf16
+ * (each enters the P.V products as three bf16 pieces whose sum is exactly
+ * p).  A row's bits depend on neither n_seq nor the other streams.  This is
+ * attn_decode_rows with one row per stream.  A row with no attended key
+ * (t < 0) gives +0.
  *
  *   out        device bf16 [S][Hq][D], written
  *   q          device bf16 [S][Hq][D]
@@ -119,6 +123,57 @@ int attn_decode(void* out, const void* q, const void* k_cache,
                 int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
                 int ring, int window, float scale, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* Largest decode window (rows per stream) of attn_decode_rows. */
+#define ATTN_DECODE_MAX_ROWS 16
+
+/*
+ * Workspace bytes attn_decode_rows needs for these sizes (device memory the
+ * caller allocates; partials of every row, head and chunk run).  Returns 0
+ * for arguments attn_decode_rows would refuse.
+ */
+size_t attn_decode_rows_workspace_bytes(int n_seq, int rows, int n_q_heads,
+                                        int head_dim, int cache_cap);
+
+/*
+ * Decode windows: `rows` consecutive rows per stream, row r of stream s at
+ * position pos[s] + r (PR #975 decode attention commits: a key head's query
+ * heads and two decode rows fill one 16-row tile, each key and value read
+ * once for the window, and every row keeps its bits at any window width;
+ * PR #1183 engine note: windows of up to 16 rows a stream).  Each row is an
+ * ordinary decode row of its position (causal, window W): the keys are the
+ * cache slots it attends, split into runs of 256-slot chunks whose partials
+ * merge in ascending order over the largest run maximum.  Probabilities stay
+ * fp32 (the P.V products take each p as three bf16 pieces whose sum is p
+ * exactly).  A row's output depends neither on `rows` nor on n_seq nor on
+ * which other rows share the call: rows = 1 gives attn_decode's bits.
+ * Every row's own key and value must already be in the cache
+ * (attn_cache_write of the window's rows first).
+ *
+ *   out        device bf16 [S][rows][Hq][D], written
+ *   q          device bf16 [S][rows][Hq][D]
+ *   k_cache    device bf16 [S][Hkv][cap][D]
+ *   v_cache    device bf16 [S][Hkv][cap][D]
+ *   pos        device int32 [S]: position of each stream's first row (read on
+ *              the device, not checked; pos[s] + rows - 1 must fit in int32)
+ *   n_seq      S >= 0 (0 launches nothing)
+ *   rows       1 .. ATTN_DECODE_MAX_ROWS
+ *   ring       0 linear cache, 1 ring of cap slots: then 1 <= W and
+ *              W + rows - 1 <= cap, so the later rows' writes leave the
+ *              first row's window in the ring
+ *   window     W >= 0, 0 = none (linear only)
+ *   scale      finite fp32 score scale
+ *   workspace  device, >= attn_decode_rows_workspace_bytes(S, rows, Hq, D,
+ *              cap) bytes, 16-byte aligned; contents on entry are ignored
+ * Errors as attn_decode, plus ATTN_E_RANGE for rows outside 1..16 and
+ * ATTN_E_WINDOW for a ring whose W is 0 or leaves fewer than rows - 1 spare
+ * slots.
+ */
+int attn_decode_rows(void* out, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* pos, int n_seq, int rows,
+                     int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
+                     int ring, int window, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 /*
  * Prompt attention for one stream's chunk of n_rows rows at positions

@@ -40,6 +40,7 @@ class Workload:
     ring: int = 0
     window: int = 0
     pos: tuple = ()
+    rows: int = 1             # decode window: rows per stream at pos .. pos + rows - 1
     # prefill
     n_rows: int = 0
     chunk: int = 0
@@ -70,6 +71,18 @@ WORKLOADS: dict[str, Workload] = {
         name="decode_global_32k", kind="decode", Hq=32, Hkv=2, D=512,
         scale=_f32(1 / math.sqrt(512)), seed=1003, S=8, cap=32768, ring=0,
         window=0, pos=tuple(32767 for _ in range(8))),
+    # decode windows of 16 rows a stream (128 rows a forward) on a global
+    # layer: 8 streams over a 32768-key linear cache, last rows at its end
+    "decode_rows_global_32k": Workload(
+        name="decode_rows_global_32k", kind="decode", Hq=32, Hkv=2, D=512,
+        scale=_f32(1 / math.sqrt(512)), seed=1006, S=8, cap=32768, ring=0,
+        window=0, pos=tuple(32752 for _ in range(8)), rows=16),
+    # ... on a sliding layer: ring of 1536 slots (window 1024 plus room for
+    # the window's later rows), streams at different ring phases
+    "decode_rows_sliding_1536": Workload(
+        name="decode_rows_sliding_1536", kind="decode", Hq=32, Hkv=4, D=256,
+        scale=_f32(1 / 16), seed=1007, S=8, cap=1536, ring=1, window=1024,
+        pos=tuple(4080 + 1000 * s for s in range(8)), rows=16),
     # sliding-layer prefill: 8192-token prompt in 128-row chunks, ring of
     # window + chunk = 1152 slots, P rounded to bf16
     "prefill_sliding_8k": Workload(
@@ -124,6 +137,17 @@ def decode_inputs(w: Workload, S: int | None = None, cap: int | None = None,
     k = randn_bf16_bits(rng, (S, w.Hkv, cap, w.D))
     v = randn_bf16_bits(rng, (S, w.Hkv, cap, w.D))
     return q, k, v, np.asarray(pos, dtype=np.int32).reshape(S)
+
+
+def decode_rows_inputs(w: Workload, S: int | None = None, seed: int | None = None):
+    """q [S][rows][Hq][D], k_cache, v_cache [S][Hkv][cap][D] (bf16 bits), pos
+    [S] int32 (first row of each window); every slot holds a written key."""
+    S = w.S if S is None else S
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    q = randn_bf16_bits(rng, (S, w.rows, w.Hq, w.D))
+    k = randn_bf16_bits(rng, (S, w.Hkv, w.cap, w.D))
+    v = randn_bf16_bits(rng, (S, w.Hkv, w.cap, w.D))
+    return q, k, v, np.asarray(w.pos[:S], dtype=np.int32)
 
 
 def prefill_inputs(w: Workload, n_rows: int | None = None, seed: int | None = None):

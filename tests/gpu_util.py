@@ -38,6 +38,20 @@ def run_decode(ga, q, k, v, pos, Hkv, ring, window, scale, ws_pad=0):
     return down(out)
 
 
+def run_decode_rows(ga, q, k, v, pos, Hkv, ring, window, scale):
+    """q [S][R][Hq][D] bf16 bits; returns out [S][R][Hq][D] bits."""
+    S, R, Hq, D = q.shape
+    cap = k.shape[2]
+    out = torch.empty((S, R, Hq, D), dtype=torch.int16, device=DEV)
+    nbytes = ga.attn_decode_rows_workspace_bytes(S, R, Hq, D, cap)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    kd = k if isinstance(k, torch.Tensor) else up(k)
+    vd = v if isinstance(v, torch.Tensor) else up(v)
+    ga.attn_decode_rows(out, up(q), kd, vd, up(np.asarray(pos, np.int32)), S, R, Hq, Hkv, D,
+                        cap, ring, window, scale, ws)
+    return down(out)
+
+
 def run_prefill(ga, q, k, v, Hkv, cap, ring, window, scale, p_mode, chunk,
                 pos0=0, caches=None, last_key=None, starts=None):
     """Prompt rows pos0.. in chunks: cache write, then attention, per chunk.

@@ -162,3 +162,39 @@ def test_prefill_edges_accepted_by_checks(ga):
 ])
 def test_cache_write_refusals(ga, kw, status):
     assert _cw(ga, **kw) == _status(status)
+
+
+def _rows(ga, **kw):
+    a = dict(out=P, q=P, k=P, v=P, pos=P, S=2, R=16, Hq=32, Hkv=2, D=512, cap=32768, ring=0,
+             window=0, scale=0.044, ws=P, ws_bytes=1 << 34)
+    a.update(kw)
+    return ga._lib.attn_decode_rows(a["out"], a["q"], a["k"], a["v"], a["pos"], a["S"], a["R"],
+                                    a["Hq"], a["Hkv"], a["D"], a["cap"], a["ring"], a["window"],
+                                    a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(R=0), "ATTN_E_RANGE"), (dict(R=17), "ATTN_E_RANGE"), (dict(R=-1), "ATTN_E_RANGE"),
+    (dict(ring=1, window=0, cap=1024), "ATTN_E_WINDOW"),
+    (dict(ring=1, window=1024, cap=1038), "ATTN_E_WINDOW"),     # W + R - 1 = 1039 slots
+    (dict(window=-1), "ATTN_E_WINDOW"),
+    (dict(out=None), "ATTN_E_NULL"), (dict(pos=None), "ATTN_E_NULL"),
+    (dict(ws=None), "ATTN_E_WORKSPACE"), (dict(ws_bytes=1000), "ATTN_E_WORKSPACE"),
+    (dict(D=128), "ATTN_E_HEAD_DIM"), (dict(Hq=34), "ATTN_E_GQA"), (dict(Hq=64), "ATTN_E_GQA"),
+    (dict(pos=P + 2), "ATTN_E_ALIGN"), (dict(q=P + 8), "ATTN_E_ALIGN"),
+    (dict(scale=float("nan")), "ATTN_E_RANGE"), (dict(cap=0), "ATTN_E_CACHE"),
+])
+def test_decode_rows_refusals(ga, kw, status):
+    assert _rows(ga, **kw) == _status(status)
+
+
+def test_decode_rows_edges_and_workspace(ga):
+    assert _rows(ga, S=0, out=None, q=None, ws=None) == 0
+    # a ring of exactly W + R - 1 slots passes the geometry check (then n_seq = 0)
+    assert _rows(ga, S=0, ring=1, window=1024, cap=1039) == 0
+    # partials of every (stream, row, head, 256-slot chunk), as S * R one-row streams
+    assert ga.attn_decode_rows_workspace_bytes(8, 16, 32, 512, 32768) == \
+        ga.attn_decode_workspace_bytes(128, 32, 512, 32768)
+    assert ga.attn_decode_rows_workspace_bytes(1, 0, 8, 256, 512) == 0
+    assert ga.attn_decode_rows_workspace_bytes(1, 17, 8, 256, 512) == 0
+    assert ga.ATTN_DECODE_MAX_ROWS == 16
