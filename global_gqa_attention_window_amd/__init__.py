@@ -27,6 +27,7 @@ ATTN_OK = 0
 ATTN_P_FP32, ATTN_P_BF16, ATTN_P_BF16X2 = 0, 1, 2
 ATTN_DECODE_CHUNK = 256
 ATTN_DECODE_MAX_ROWS = 16
+ATTN_DECODE_COUNTER_BYTES = 65536
 
 _c_int, _c_void_p, _c_float, _c_size_t = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
 
@@ -39,6 +40,10 @@ _lib.attn_decode_rows_workspace_bytes.argtypes = [_c_int] * 5
 _lib.attn_decode_rows.restype = _c_int
 _lib.attn_decode_rows.argtypes = ([_c_void_p] * 5 + [_c_int] * 8 +
                                   [_c_float, _c_void_p, _c_size_t, _c_void_p])
+_lib.attn_decode_rows_fused.restype = _c_int
+_lib.attn_decode_rows_fused.argtypes = _lib.attn_decode_rows.argtypes
+_lib.attn_decode_workspace_init.restype = _c_int
+_lib.attn_decode_workspace_init.argtypes = [_c_void_p, _c_size_t, _c_void_p]
 _lib.attn_prefill.restype = _c_int
 _lib.attn_prefill.argtypes = ([_c_void_p] * 4 + [_c_int] * 8 + [_c_float, _c_int, _c_void_p, _c_void_p])
 _lib.attn_cache_write.restype = _c_int
@@ -125,6 +130,27 @@ def attn_decode_rows(out, q, k_cache, v_cache, pos, n_seq, rows, n_q_heads, n_kv
                                window, float(scale), _ptr(workspace), int(workspace_bytes),
                                _stream(stream))
     _ok(st, "attn_decode_rows")
+
+
+def attn_decode_rows_fused(out, q, k_cache, v_cache, pos, n_seq, rows, n_q_heads, n_kv_heads,
+                           head_dim, cache_cap, ring, window, scale, workspace,
+                           workspace_bytes=None, stream=None) -> None:
+    """attn_decode_rows in one launch where it can; the workspace starts with
+    ATTN_DECODE_COUNTER_BYTES of counters set up by attn_decode_workspace_init."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.attn_decode_rows_fused(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(pos), n_seq, rows, n_q_heads, n_kv_heads, head_dim,
+                                     cache_cap, ring, window, float(scale), _ptr(workspace),
+                                     int(workspace_bytes), _stream(stream))
+    _ok(st, "attn_decode_rows_fused")
+
+
+def attn_decode_workspace_init(workspace, workspace_bytes=None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _ok(_lib.attn_decode_workspace_init(_ptr(workspace), int(workspace_bytes), _stream(stream)),
+        "attn_decode_workspace_init")
 
 
 def attn_prefill(out, q, k_cache, v_cache, pos0, n_rows, n_q_heads, n_kv_heads,

@@ -107,11 +107,12 @@ size_t attn_decode_rows_workspace_bytes(int n_seq, int rows, int n_q_heads, int 
     return attn_decode_workspace_bytes(n_seq * rows, n_q_heads, head_dim, cache_cap);
 }
 
-int attn_decode_rows(void* out, const void* q, const void* k_cache,
-                     const void* v_cache, const int32_t* pos, int n_seq, int rows,
-                     int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
-                     int ring, int window, float scale, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+namespace {
+
+int decode_rows_call(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* pos, int n_seq, int rows, int n_q_heads, int n_kv_heads,
+                     int head_dim, int cache_cap, int ring, int window, float scale,
+                     void* workspace, size_t workspace_bytes, bool fused, void* stream) {
     int st = check_heads(n_q_heads, n_kv_heads, head_dim);
     if (st != ATTN_OK) return st;
     if (n_seq < 0 || rows < 1 || rows > ATTN_DECODE_MAX_ROWS || (ring != 0 && ring != 1) ||
@@ -123,6 +124,9 @@ int attn_decode_rows(void* out, const void* q, const void* k_cache,
     if (tensor_bytes(n_seq, n_kv_heads, cache_cap, head_dim) < 0 ||
         tensor_bytes((long long)n_seq * rows, n_q_heads, 1, head_dim) < 0)
         return ATTN_E_RANGE;
+    // four counters per (stream, KV head) in the fused counter area
+    if (fused && (long long)n_seq * n_kv_heads * 4 * 4 > ATTN_DECODE_COUNTER_BYTES)
+        return ATTN_E_RANGE;
     if (n_seq == 0) return ATTN_OK;
     if (!out || !q || !k_cache || !v_cache || !pos) return ATTN_E_NULL;
     if (!workspace) return ATTN_E_WORKSPACE;
@@ -133,7 +137,7 @@ int attn_decode_rows(void* out, const void* q, const void* k_cache,
     const size_t need =
         attn_decode_rows_workspace_bytes(n_seq, rows, n_q_heads, head_dim, cache_cap);
     if (need == 0) return ATTN_E_RANGE;
-    if (workspace_bytes < need) return ATTN_E_WORKSPACE;
+    if (workspace_bytes < need + (fused ? ATTN_DECODE_COUNTER_BYTES : 0)) return ATTN_E_WORKSPACE;
     if (n_seq > 65535 || n_kv_heads > 65535 ||
         (cache_cap + ATTN_DECODE_CHUNK - 1) / ATTN_DECODE_CHUNK > 0x7FFFFFFF / 2)
         return ATTN_E_RANGE;
@@ -141,7 +145,37 @@ int attn_decode_rows(void* out, const void* q, const void* k_cache,
         static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
         static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
         pos, n_seq, rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring, window,
-        scale, workspace, static_cast<hipStream_t>(stream));
+        scale, workspace, fused, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+}  // namespace
+
+int attn_decode_rows(void* out, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* pos, int n_seq, int rows,
+                     int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
+                     int ring, int window, float scale, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    return decode_rows_call(out, q, k_cache, v_cache, pos, n_seq, rows, n_q_heads, n_kv_heads,
+                            head_dim, cache_cap, ring, window, scale, workspace,
+                            workspace_bytes, false, stream);
+}
+
+int attn_decode_rows_fused(void* out, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* pos, int n_seq, int rows,
+                           int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
+                           int ring, int window, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return decode_rows_call(out, q, k_cache, v_cache, pos, n_seq, rows, n_q_heads, n_kv_heads,
+                            head_dim, cache_cap, ring, window, scale, workspace,
+                            workspace_bytes, true, stream);
+}
+
+int attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+    if (!workspace) return ATTN_E_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_E_ALIGN;
+    if (workspace_bytes < ATTN_DECODE_COUNTER_BYTES) return ATTN_E_WORKSPACE;
+    const hipError_t e = launch_decode_counters_init(workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 

@@ -63,7 +63,15 @@ int decode_run_chunks(int cap) {
 }
 constexpr int WPAD = 16;       // LDS padding elements per row (per row pair at 256)
 
-template <int D, int DS>
+// Merge width: the merge kernel's waves per (row, head) and d slice; a
+// workgroup that merges in place mirrors its summation order.
+constexpr int MW = 16;
+
+// FUSE: one launch.  With one run the workgroup writes the output itself
+// (its weight e^(m - m) is 1); otherwise the last workgroup of a (stream, KV
+// head, column group) to finish, found by a counter that it resets, merges
+// that group's rows in the merge kernel's order, so the bits do not change.
+template <int D, int DS, bool FUSE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_rows_kernel(const uint16_t* __restrict__ q,
                         const uint16_t* __restrict__ kc,
@@ -71,6 +79,8 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
                         const int32_t* __restrict__ pos,
                         float* __restrict__ part_acc,
                         float* __restrict__ part_ml,
+                        uint16_t* __restrict__ out,
+                        uint32_t* __restrict__ counters,
                         int R, int Hq, int Hkv, int G, int RPT, int NT, int CG,
                         int n_items, int cap, int nrun, int cpr, int ring, int window,
                         float c) {
@@ -153,14 +163,14 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
             bb_hi = b0 + (63 - __builtin_clzll(bal)) / 8;
         }
     }
-    if (bb_hi < 0) {
-        if (cv && dp == 0 && grp == 0) {
-            part_ml[2 * pidx + 0] = -INFINITY;
-            part_ml[2 * pidx + 1] = 0.f;
-        }
-        return;
-    }
+    f32x4 acc[DTW];
+#pragma unroll
+    for (int dt = 0; dt < DTW; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
 
+    // a run with no attended key leaves an empty partial (m = -inf, l = 0)
+    if (bb_hi >= 0) {
     // Q^T operand in AGPRs: Q[column][32 st + 8 grp .. +7]
     u32x4 qreg[QST];
     {
@@ -196,12 +206,6 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         slot = attended(slot, t1, t1m, w_all) ? slot : sub;
         dma16_asm(base + (size_t)slot * D + (lane % LPR) * 8, lds_addr(stage + dma_dst[k]));
     };
-
-    f32x4 acc[DTW];
-#pragma unroll
-    for (int dt = 0; dt < DTW; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
 
     const int kofs = row_pos<D, WPAD>(col) + 8 * grp;
     // V^T operand: lane j of a 16-lane group points at the row of k-slot
@@ -330,17 +334,129 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         if (b < bb_hi) block(b, (b - bb_lo) & 1, std::true_type{});
         else block(b, (b - bb_lo) & 1, std::false_type{});
     }
+    }
 
     const float l_tot = xsum4(l_run);
-    if (!cv) return;
-    if (dp == 0 && grp == 0) {
-        part_ml[2 * pidx + 0] = m_run;
-        part_ml[2 * pidx + 1] = l_tot;
-    }
     // lane holds d = dp D / DS + 16 dt + 4 grp + i of its column in acc[dt][i]
-    float* dst = part_acc + pidx * D + dp * (D / DS) + 4 * grp;
+    const int dofs = dp * (D / DS) + 4 * grp;
+    uint16_t* orow = out + (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * D + dofs;
+    auto store_out = [&](const f32x4 (&o)[DTW], float l) {
 #pragma unroll
-    for (int dt = 0; dt < DTW; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = acc[dt];
+        for (int dt = 0; dt < DTW; ++dt) {
+            uint32_t bb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                bb[i] = (l != 0.f || l != l) ? f32_to_bf16_bits(o[dt][i] / l) : 0u;
+            *reinterpret_cast<u32x2*>(orow + 16 * dt) =
+                u32x2{pack_bf16x2(bb[0], bb[1]), pack_bf16x2(bb[2], bb[3])};
+        }
+    };
+    if constexpr (FUSE) {
+        if (nrun == 1) {
+            if (cv) store_out(acc, l_tot);
+            return;
+        }
+    }
+    if (cv) {
+        if (dp == 0 && grp == 0) {
+            part_ml[2 * pidx + 0] = m_run;
+            part_ml[2 * pidx + 1] = l_tot;
+        }
+        float* dst = part_acc + pidx * D + dofs;
+#pragma unroll
+        for (int dt = 0; dt < DTW; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = acc[dt];
+    }
+    if constexpr (FUSE) {
+        // publish this run's partials, count the run; the last run's
+        // workgroup merges (and leaves the counter at zero for the next call)
+        // (the barrier orders every wave's stores before thread 0's release,
+        // and thread 0's acquire before every wave's loads: one cache
+        // write-back and one invalidate per workgroup)
+        __shared__ int s_last;
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t* ctr = counters + ((size_t)s * Hkv + g) * CG + cgi;
+            const uint32_t old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+            const int last = old == (uint32_t)(nrun - 1);
+            if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = last;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        if (!cv) return;
+        {
+            // the merge kernel's arithmetic for nrun <= MW: M the largest run
+            // maximum; each run's weighted sums round once (wt l and wt acc,
+            // from zero) and add in ascending run order (the merge kernel's
+            // waves hold one run or none, and adding its empty waves' zeros
+            // changes nothing: no sum here is -0).  A run with m = -inf adds
+            // zero (its partial holds zeros), so every load can go out at once
+#pragma clang fp contract(off)
+            const size_t base = (pidx - run);
+            const float2* mlp = reinterpret_cast<const float2*>(part_ml) + base;
+            float2 e[MW];
+#pragma unroll
+            for (int ci = 0; ci < MW; ++ci) e[ci] = mlp[min(ci, nrun - 1)];
+            float M = -INFINITY;
+#pragma unroll
+            for (int ci = 0; ci < MW; ++ci) M = fmaxf(M, e[ci].x);
+            // weights of the runs (0 for runs past nrun or with m = -inf)
+            float wts[MW];
+            float Lt = 0.f;
+#pragma unroll
+            for (int ci = 0; ci < MW; ++ci) {
+                const bool use = ci < nrun && e[ci].x != -INFINITY;
+                wts[ci] = use ? fast_exp2(e[ci].x - M) : 0.f;
+                const float lw = wts[ci] * (use ? e[ci].y : 0.f);
+                Lt = Lt + lw;
+            }
+            // d tiles in groups of DG, runs' accumulators loaded CB at a time
+            constexpr int DG = DTW < 8 ? DTW : 8;
+            constexpr int CB = 16 / DG;
+#pragma unroll
+            for (int d0 = 0; d0 < DTW; d0 += DG) {
+                f32x4 ot[DG];
+#pragma unroll
+                for (int j = 0; j < DG; ++j) ot[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (M != -INFINITY) {
+#pragma unroll
+                    for (int c0 = 0; c0 < MW; c0 += CB) {
+                        if (c0 >= nrun) break;
+                        f32x4 av[CB][DG];
+#pragma unroll
+                        for (int u = 0; u < CB; ++u) {
+                            const float* a = part_acc + (base + min(c0 + u, nrun - 1)) * D + dofs;
+#pragma unroll
+                            for (int j = 0; j < DG; ++j)
+                                av[u][j] = *reinterpret_cast<const f32x4*>(a + 16 * (d0 + j));
+                        }
+#pragma unroll
+                        for (int u = 0; u < CB; ++u) {
+                            const int ci = c0 + u;
+                            const bool use = ci < nrun && e[ci].x != -INFINITY;
+#pragma unroll
+                            for (int j = 0; j < DG; ++j)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    const float ow = wts[ci] * (use ? av[u][j][i] : 0.f);
+                                    ot[j][i] = ot[j][i] + ow;
+                                }
+                        }
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < DG; ++j) {
+                    uint32_t bb[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        bb[i] = (Lt != 0.f || Lt != Lt) ? f32_to_bf16_bits(ot[j][i] / Lt) : 0u;
+                    *reinterpret_cast<u32x2*>(orow + 16 * (d0 + j)) =
+                        u32x2{pack_bf16x2(bb[0], bb[1]), pack_bf16x2(bb[2], bb[3])};
+                }
+            }
+        }
+    }
 }
 
 // Merge of chunk partials in ascending chunk order.  A block of MW waves
@@ -349,8 +465,6 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
 // then the waves' sums are added in ascending wave order.  M is the largest
 // chunk maximum; chunks with no attended key (m = -inf) are skipped, never
 // multiplied; out = bf16(sum e^(m_c - M) acc_c / sum e^(m_c - M) l_c).
-constexpr int MW = 16;
-
 template <int D>
 __global__ __launch_bounds__(64 * MW)
 void decode_merge_kernel(uint16_t* __restrict__ out,
@@ -438,7 +552,7 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                          float scale, void* ws, hipStream_t stream) {
     // one row per stream is a window of one row: the same kernel and bits
     return launch_decode_rows(out, q, kc, vc, pos, S, 1, Hq, Hkv, D, cap, ring, window, scale,
-                              ws, stream);
+                              ws, false, stream);
 }
 
 static hipError_t launch_decode_merge(uint16_t* out, const float* part_acc, const float* part_ml,
@@ -454,7 +568,7 @@ static hipError_t launch_decode_merge(uint16_t* out, const float* part_acc, cons
 hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                               const uint16_t* vc, const int32_t* pos, int S, int R, int Hq,
                               int Hkv, int D, int cap, int ring, int window, float scale,
-                              void* ws, hipStream_t stream) {
+                              void* ws, bool fused, hipStream_t stream) {
     const int G = Hq / Hkv;
     const int RPT = 16 / G;                      // rows per 16-column tile
     const int NT = (R + RPT - 1) / RPT;          // column tiles of a window
@@ -469,24 +583,46 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
     const long long n_items = (long long)nrun * Hkv * S;
     const long long nwg = (n_items + 7) / 8 * 8 * CG;
     if (nwg > 0x7FFFFFFFLL || (long long)S * R * Hq > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    float* part_acc = reinterpret_cast<float*>(ws);
+    // one launch when the merge fits a workgroup (at most MW runs); the
+    // counters sit at the start of a fused call's workspace
+    const bool one = fused && nrun <= MW;
+    uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
+    float* part_acc = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                               (fused ? ATTN_DECODE_COUNTER_BYTES : 0));
     float* part_ml = part_acc + (size_t)S * R * Hq * nrun * D;
     const float c = scale * ATTN_LOG2E;
-#define ROWS_LAUNCH(DD, SS)                                                                   \
-    decode_rows_kernel<DD, SS><<<(unsigned)nwg, 256, 0, stream>>>(                            \
-        q, kc, vc, pos, part_acc, part_ml, R, Hq, Hkv, G, RPT, NT, CG, (int)n_items, cap,     \
-        nrun, cpr, ring, window, c)
+#define ROWS_LAUNCH(DD, SS, FF)                                                               \
+    decode_rows_kernel<DD, SS, FF><<<(unsigned)nwg, 256, 0, stream>>>(                        \
+        q, kc, vc, pos, part_acc, part_ml, out, counters, R, Hq, Hkv, G, RPT, NT, CG,         \
+        (int)n_items, cap, nrun, cpr, ring, window, c)
+#define ROWS_DS(DD, FF)                                                                       \
+    do {                                                                                      \
+        if (DS == 4) ROWS_LAUNCH(DD, 4, FF);                                                  \
+        else if (DS == 2) ROWS_LAUNCH(DD, 2, FF);                                             \
+        else ROWS_LAUNCH(DD, 1, FF);                                                          \
+    } while (0)
     if (D == 256) {
-        if (DS == 4) ROWS_LAUNCH(256, 4);
-        else if (DS == 2) ROWS_LAUNCH(256, 2);
-        else ROWS_LAUNCH(256, 1);
+        if (one) ROWS_DS(256, true);
+        else ROWS_DS(256, false);
     } else {
-        if (DS == 4) ROWS_LAUNCH(512, 4);
-        else if (DS == 2) ROWS_LAUNCH(512, 2);
-        else ROWS_LAUNCH(512, 1);
+        if (one) ROWS_DS(512, true);
+        else ROWS_DS(512, false);
     }
+#undef ROWS_DS
 #undef ROWS_LAUNCH
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || one) return e;
     return launch_decode_merge(out, part_acc, part_ml, S * R * Hq, D, nrun, stream);
+}
+
+// zero fill of a fused decode's counter area (a kernel, so a graph may hold it)
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_decode_counters_init(void* ws, hipStream_t stream) {
+    constexpr int n = ATTN_DECODE_COUNTER_BYTES / 4;
+    zero_words_kernel<<<(n + 255) / 256, 256, 0, stream>>>(static_cast<uint32_t*>(ws), n);
+    return hipGetLastError();
 }

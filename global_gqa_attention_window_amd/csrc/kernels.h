@@ -17,10 +17,13 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* kc,
 
 // R rows per stream at positions pos[s] .. pos[s] + R - 1 (1 <= R <= 16);
 // q, out [S][R][Hq][D]; ws as decode_workspace_bytes(S * R, Hq, D, cap)
+// fused: one launch where the merge fits a workgroup; ws then starts with
+// ATTN_DECODE_COUNTER_BYTES of counters (zero on entry, left zero)
 hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                               const uint16_t* vc, const int32_t* pos, int S, int R, int Hq,
                               int Hkv, int D, int cap, int ring, int window, float scale,
-                              void* ws, hipStream_t stream);
+                              void* ws, bool fused, hipStream_t stream);
+hipError_t launch_decode_counters_init(void* ws, hipStream_t stream);
 
 int prefill_key_block(int D, int p_mode);
 

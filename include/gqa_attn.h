@@ -175,6 +175,43 @@ int attn_decode_rows(void* out, const void* q, const void* k_cache,
                      int ring, int window, float scale, void* workspace,
                      size_t workspace_bytes, void* stream);
 
+/* Bytes at the start of a fused decode's workspace that hold its counters. */
+#define ATTN_DECODE_COUNTER_BYTES 65536
+
+/*
+ * attn_decode_rows in one launch where it can (PR #975 decode commits: with
+ * one key chunk the partial writes the merged output itself, e^(top - top)
+ * being 1; the Gemma 4 CUDA engine note in PR #1183: a decode forward's
+ * launches depend on its row count alone, positions read on the device, so
+ * each row count is captured once as a graph and replayed).  With one run
+ * per (stream, KV head) the kernel writes the output directly; with up to 16
+ * runs the last workgroup to finish merges, in the merge kernel's order;
+ * beyond that it is attn_decode_rows (partials, then the merge).  Outputs
+ * are bit for bit those of attn_decode_rows.  Nothing is allocated and no
+ * memset is issued, so a graph may capture the call.
+ *
+ * Arguments as attn_decode_rows, except the workspace: at least
+ * ATTN_DECODE_COUNTER_BYTES + attn_decode_rows_workspace_bytes(...) bytes,
+ * whose first ATTN_DECODE_COUNTER_BYTES must be zero on entry (set once by
+ * attn_decode_workspace_init; every call leaves them zero).  Calls that
+ * share a workspace must not overlap.  ATTN_E_RANGE when n_seq * Hkv >
+ * 4096 (the counter area's limit).
+ */
+int attn_decode_rows_fused(void* out, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* pos, int n_seq, int rows,
+                           int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
+                           int ring, int window, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * Zeroes the counter area (first ATTN_DECODE_COUNTER_BYTES) of a workspace
+ * for attn_decode_rows_fused, by a kernel on `stream`.  Needed once per
+ * workspace, and again after the workspace served anything else.
+ * ATTN_E_WORKSPACE for a NULL or smaller workspace, ATTN_E_ALIGN unless
+ * 16-byte aligned.
+ */
+int attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Prompt attention for one stream's chunk of n_rows rows at positions
  * pos0 .. pos0 + n_rows - 1 (PR #975 prompt attention commits; PR #1183

@@ -198,3 +198,20 @@ def test_decode_rows_edges_and_workspace(ga):
     assert ga.attn_decode_rows_workspace_bytes(1, 0, 8, 256, 512) == 0
     assert ga.attn_decode_rows_workspace_bytes(1, 17, 8, 256, 512) == 0
     assert ga.ATTN_DECODE_MAX_ROWS == 16
+
+
+def test_fused_decode_refusals(ga):
+    lib = ga._lib
+    n = 1 << 34
+    # counter area beyond its limit (n_seq * Hkv > 4096)
+    assert lib.attn_decode_rows_fused(P, P, P, P, P, 4097, 1, 8, 1, 256, 512, 0, 0, 0.1, P, n,
+                                      None) == _status("ATTN_E_RANGE")
+    # workspace without room for the counters
+    need = ga.attn_decode_rows_workspace_bytes(1, 1, 8, 256, 512)
+    assert lib.attn_decode_rows_fused(P, P, P, P, P, 1, 1, 8, 1, 256, 512, 0, 0, 0.1, P, need,
+                                      None) == _status("ATTN_E_WORKSPACE")
+    assert lib.attn_decode_rows_fused(P, P, P, P, P, 0, 1, 8, 1, 256, 512, 0, 0, 0.1, None, 0,
+                                      None) == 0
+    assert lib.attn_decode_workspace_init(None, 1 << 20, None) == _status("ATTN_E_WORKSPACE")
+    assert lib.attn_decode_workspace_init(P, 1000, None) == _status("ATTN_E_WORKSPACE")
+    assert lib.attn_decode_workspace_init(P + 4, 1 << 20, None) == _status("ATTN_E_ALIGN")
