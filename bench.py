@@ -10,6 +10,8 @@ Prints one JSON line: whole-step tokens/s (prompt tokens + the decode token),
 the prefill kernel against the bf16 matrix-core roofline (duration from HIP
 events recorded on the launch stream around every prefill launch), the decode
 kernels against HBM bandwidth, and the CPU oracle timed on a bounded sample.
+Apart from the step, decode windows (16 rows a stream, 8 streams, 32768 keys)
+are timed against the bf16 matrix-core peak.
 """
 from __future__ import annotations
 
@@ -79,6 +81,46 @@ def traffic_from_profile(kernel_src: str):
         return None
     sha = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()
     return float(m_b.group(1)) if sha == m_sha.group(1) else None
+
+
+def decode_windows(ga, torch, dev, iters: int = 10):
+    """Decode windows of 16 rows a stream, 8 streams (128 rows), over a
+    32768-key global-layer cache, timed apart from the step (HIP events on
+    the launch stream): algorithmic flops 4 D per (row, head, attended key),
+    K/V bytes once per (stream, KV head)."""
+    from synthetic.gen import WORKLOADS
+    w = WORKLOADS["decode_rows_global_32k"]
+    S, R = w.S, w.rows
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    q = torch.randn((S, R, w.Hq, w.D), generator=g, device=dev, dtype=torch.bfloat16)
+    kc = torch.randn((S, w.Hkv, w.cap, w.D), generator=g, device=dev, dtype=torch.bfloat16)
+    vc = torch.randn((S, w.Hkv, w.cap, w.D), generator=g, device=dev, dtype=torch.bfloat16)
+    pos = torch.tensor(w.pos, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(ga.attn_decode_rows_workspace_bytes(S, R, w.Hq, w.D, w.cap),
+                     dtype=torch.uint8, device=dev)
+
+    def call():
+        ga.attn_decode_rows(out, q, kc, vc, pos, S, R, w.Hq, w.Hkv, w.D, w.cap, w.ring,
+                            w.window, w.scale, ws)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    pairs = sum(int(p) + r + 1 for p in w.pos for r in range(R))     # (row, key) attended
+    flops = 4 * w.D * w.Hq * pairs
+    kv_bytes = 2 * S * w.Hkv * w.cap * w.D * 2
+    tf = flops / (us * 1e-6) / 1e12
+    return {"workload": w.name, "streams": S, "rows_per_stream": R, "cache_keys": w.cap,
+            "us": round(us, 1), "rows_per_s": round(S * R / (us * 1e-6), 1),
+            "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "kv_GB/s": round(kv_bytes / (us * 1e-6) / 1e9, 1)}
 
 
 def cpu_baseline(q, k, v, w, n_rows_sample: int):
@@ -221,6 +263,9 @@ def main():
         "decode": {"us": round(dec_us, 2), "GB/s": round(dec_gbs, 1),
                    "frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4), "bytes": dec_bytes},
     }
+    del q, k, v, kc, vc, out, dk, dv
+    torch.cuda.empty_cache()
+    rec["decode_windows"] = decode_windows(ga, torch, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, w, args.cpu_rows)
     print(json.dumps(rec), flush=True)
