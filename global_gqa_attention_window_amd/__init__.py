@@ -44,6 +44,13 @@ _lib.attn_decode_rows_fused.restype = _c_int
 _lib.attn_decode_rows_fused.argtypes = _lib.attn_decode_rows.argtypes
 _lib.attn_decode_workspace_init.restype = _c_int
 _lib.attn_decode_workspace_init.argtypes = [_c_void_p, _c_size_t, _c_void_p]
+_lib.attn_qkv_prep.restype = _c_int
+_lib.attn_qkv_prep.argtypes = ([_c_void_p] * 7 + [_c_float, _c_int, _c_void_p] + [_c_int] * 6 +
+                               [_c_void_p])
+_lib.attn_decode_prep_fused.restype = _c_int
+_lib.attn_decode_prep_fused.argtypes = ([_c_void_p] * 5 + [_c_float, _c_int] + [_c_void_p] * 3 +
+                                        [_c_int] * 7 + [_c_float, _c_void_p, _c_size_t,
+                                                        _c_void_p])
 _lib.attn_prefill.restype = _c_int
 _lib.attn_prefill.argtypes = ([_c_void_p] * 4 + [_c_int] * 8 + [_c_float, _c_int, _c_void_p, _c_void_p])
 _lib.attn_cache_write.restype = _c_int
@@ -144,6 +151,33 @@ def attn_decode_rows_fused(out, q, k_cache, v_cache, pos, n_seq, rows, n_q_heads
                                      cache_cap, ring, window, float(scale), _ptr(workspace),
                                      int(workspace_bytes), _stream(stream))
     _ok(st, "attn_decode_rows_fused")
+
+
+def attn_qkv_prep(q_out, k_cache, v_cache, qkv, q_norm_w, k_norm_w, inv_freq, eps, v_norm,
+                  pos, n_seq, n_q_heads, n_kv_heads, head_dim, cache_cap, ring,
+                  stream=None) -> None:
+    """qkv [S][(Hq + 2 Hkv) D] bf16 -> q_out [S][Hq][D], key/value at each
+    row's cache slot; inv_freq fp32 [D/2]."""
+    st = _lib.attn_qkv_prep(_ptr(q_out), _ptr(k_cache), _ptr(v_cache), _ptr(qkv),
+                            _ptr(q_norm_w), _ptr(k_norm_w), _ptr(inv_freq), float(eps),
+                            int(v_norm), _ptr(pos), n_seq, n_q_heads, n_kv_heads, head_dim,
+                            cache_cap, ring, _stream(stream))
+    _ok(st, "attn_qkv_prep")
+
+
+def attn_decode_prep_fused(out, qkv, q_norm_w, k_norm_w, inv_freq, eps, v_norm, k_cache,
+                           v_cache, pos, n_seq, n_q_heads, n_kv_heads, head_dim, cache_cap,
+                           ring, window, scale, workspace, workspace_bytes=None,
+                           stream=None) -> None:
+    """attn_qkv_prep + one-row attn_decode_rows_fused in the decode kernel."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.attn_decode_prep_fused(_ptr(out), _ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w),
+                                     _ptr(inv_freq), float(eps), int(v_norm), _ptr(k_cache),
+                                     _ptr(v_cache), _ptr(pos), n_seq, n_q_heads, n_kv_heads,
+                                     head_dim, cache_cap, ring, window, float(scale),
+                                     _ptr(workspace), int(workspace_bytes), _stream(stream))
+    _ok(st, "attn_decode_prep_fused")
 
 
 def attn_decode_workspace_init(workspace, workspace_bytes=None, stream=None) -> None:

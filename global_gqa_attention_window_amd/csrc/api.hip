@@ -109,10 +109,22 @@ size_t attn_decode_rows_workspace_bytes(int n_seq, int rows, int n_q_heads, int 
 
 namespace {
 
+// checks of the prologue's own arguments (stacked rows, scales, frequencies)
+int check_prep(const PrepArgs& pa) {
+    if (!pa.qkv || !pa.q_w || !pa.k_w || !pa.inv_freq) return ATTN_E_NULL;
+    if (!aligned16(pa.qkv) || !aligned16(pa.q_w) || !aligned16(pa.k_w) ||
+        (reinterpret_cast<uintptr_t>(pa.inv_freq) & 3u) != 0)
+        return ATTN_E_ALIGN;
+    if (!isfinite(pa.eps) || pa.eps < 0.f || (pa.v_norm != 0 && pa.v_norm != 1))
+        return ATTN_E_RANGE;
+    return ATTN_OK;
+}
+
 int decode_rows_call(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* pos, int n_seq, int rows, int n_q_heads, int n_kv_heads,
                      int head_dim, int cache_cap, int ring, int window, float scale,
-                     void* workspace, size_t workspace_bytes, bool fused, void* stream) {
+                     void* workspace, size_t workspace_bytes, bool fused,
+                     const PrepArgs* prep, void* stream) {
     int st = check_heads(n_q_heads, n_kv_heads, head_dim);
     if (st != ATTN_OK) return st;
     if (n_seq < 0 || rows < 1 || rows > ATTN_DECODE_MAX_ROWS || (ring != 0 && ring != 1) ||
@@ -128,6 +140,11 @@ int decode_rows_call(void* out, const void* q, const void* k_cache, const void* 
     if (fused && (long long)n_seq * n_kv_heads * 4 * 4 > ATTN_DECODE_COUNTER_BYTES)
         return ATTN_E_RANGE;
     if (n_seq == 0) return ATTN_OK;
+    if (prep) {
+        st = check_prep(*prep);
+        if (st != ATTN_OK) return st;
+        q = prep->qkv;                           // the queries come from the stacked rows
+    }
     if (!out || !q || !k_cache || !v_cache || !pos) return ATTN_E_NULL;
     if (!workspace) return ATTN_E_WORKSPACE;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
@@ -145,7 +162,7 @@ int decode_rows_call(void* out, const void* q, const void* k_cache, const void* 
         static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
         static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
         pos, n_seq, rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring, window,
-        scale, workspace, fused, static_cast<hipStream_t>(stream));
+        scale, workspace, fused, prep, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
@@ -158,7 +175,7 @@ int attn_decode_rows(void* out, const void* q, const void* k_cache,
                      size_t workspace_bytes, void* stream) {
     return decode_rows_call(out, q, k_cache, v_cache, pos, n_seq, rows, n_q_heads, n_kv_heads,
                             head_dim, cache_cap, ring, window, scale, workspace,
-                            workspace_bytes, false, stream);
+                            workspace_bytes, false, nullptr, stream);
 }
 
 int attn_decode_rows_fused(void* out, const void* q, const void* k_cache,
@@ -168,7 +185,48 @@ int attn_decode_rows_fused(void* out, const void* q, const void* k_cache,
                            size_t workspace_bytes, void* stream) {
     return decode_rows_call(out, q, k_cache, v_cache, pos, n_seq, rows, n_q_heads, n_kv_heads,
                             head_dim, cache_cap, ring, window, scale, workspace,
-                            workspace_bytes, true, stream);
+                            workspace_bytes, true, nullptr, stream);
+}
+
+int attn_decode_prep_fused(void* out, const void* qkv, const void* q_norm_w,
+                           const void* k_norm_w, const float* inv_freq, float eps, int v_norm,
+                           void* k_cache, void* v_cache, const int32_t* pos, int n_seq,
+                           int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
+                           int ring, int window, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    const PrepArgs pa = {static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(q_norm_w),
+                         static_cast<const uint16_t*>(k_norm_w), inv_freq, eps, v_norm,
+                         static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache)};
+    return decode_rows_call(out, qkv, k_cache, v_cache, pos, n_seq, 1, n_q_heads, n_kv_heads,
+                            head_dim, cache_cap, ring, window, scale, workspace,
+                            workspace_bytes, true, &pa, stream);
+}
+
+int attn_qkv_prep(void* q_out, void* k_cache, void* v_cache, const void* qkv,
+                  const void* q_norm_w, const void* k_norm_w, const float* inv_freq, float eps,
+                  int v_norm, const int32_t* pos, int n_seq, int n_q_heads, int n_kv_heads,
+                  int head_dim, int cache_cap, int ring, void* stream) {
+    int st = check_heads(n_q_heads, n_kv_heads, head_dim);
+    if (st != ATTN_OK) return st;
+    if (n_seq < 0 || (ring != 0 && ring != 1)) return ATTN_E_RANGE;
+    if (cache_cap < 1) return ATTN_E_CACHE;
+    if (tensor_bytes(n_seq, n_kv_heads, cache_cap, head_dim) < 0 ||
+        tensor_bytes(n_seq, n_q_heads + 2LL * n_kv_heads, 1, head_dim) < 0 || n_seq > 65535)
+        return ATTN_E_RANGE;
+    if (n_seq == 0) return ATTN_OK;
+    const PrepArgs pa = {static_cast<const uint16_t*>(qkv), static_cast<const uint16_t*>(q_norm_w),
+                         static_cast<const uint16_t*>(k_norm_w), inv_freq, eps, v_norm,
+                         static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache)};
+    st = check_prep(pa);
+    if (st != ATTN_OK) return st;
+    if (!q_out || !k_cache || !v_cache || !pos) return ATTN_E_NULL;
+    if (!aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        (reinterpret_cast<uintptr_t>(pos) & 3u) != 0)
+        return ATTN_E_ALIGN;
+    const hipError_t e = launch_qkv_prep(static_cast<uint16_t*>(q_out), pa, pos, n_seq,
+                                         n_q_heads, n_kv_heads, head_dim, cache_cap, ring,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
 int attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {

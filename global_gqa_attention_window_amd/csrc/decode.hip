@@ -14,6 +14,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "prologue.h"
 
 namespace {
 
@@ -71,7 +72,11 @@ constexpr int MW = 16;
 // (its weight e^(m - m) is 1); otherwise the last workgroup of a (stream, KV
 // head, column group) to finish, found by a counter that it resets, merges
 // that group's rows in the merge kernel's order, so the bits do not change.
-template <int D, int DS, bool FUSE>
+// PREP (one row per stream): the queries come from the stacked projection
+// row, normed and rotated in place, and the workgroup whose run holds the
+// row's slot first writes the row's normed, rotated key and its value there
+// (the functions of prologue.h, so the bits equal the standalone prologue).
+template <int D, int DS, bool FUSE, bool PREP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_rows_kernel(const uint16_t* __restrict__ q,
                         const uint16_t* __restrict__ kc,
@@ -83,7 +88,7 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
                         uint32_t* __restrict__ counters,
                         int R, int Hq, int Hkv, int G, int RPT, int NT, int CG,
                         int n_items, int cap, int nrun, int cpr, int ring, int window,
-                        float c) {
+                        float c, PrepArgs pa) {
     constexpr int WC = 4 / DS;                  // column tiles per workgroup
     constexpr int QST = D / 32;                 // reduction steps of a score
     constexpr int DTW = D / 16 / DS;            // 16-wide d tiles of this wave
@@ -100,6 +105,8 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
 
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][BLK];
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][BLK];
+    // the row's new key and value (PREP)
+    __shared__ __attribute__((aligned(16))) uint16_t kv_new[PREP ? 2 : 1][PREP ? D : 8];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -171,19 +178,6 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
 
     // a run with no attended key leaves an empty partial (m = -inf, l = 0)
     if (bb_hi >= 0) {
-    // Q^T operand in AGPRs: Q[column][32 st + 8 grp .. +7]
-    u32x4 qreg[QST];
-    {
-        const uint16_t* qrow = q + (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * D + 8 * grp;
-#pragma unroll
-        for (int st = 0; st < QST; ++st) {
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            qreg[st] = cv ? ld16(qrow + 32 * st) : z;
-        }
-#pragma unroll
-        for (int st = 0; st < QST; ++st) asm volatile("" : "+a"(qreg[st]));
-    }
-
     const size_t head_base = ((size_t)s * Hkv + g) * (size_t)cap * D;
     const uint16_t* Kh = kc + head_base;
     const uint16_t* Vh = vc + head_base;
@@ -206,6 +200,51 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         slot = attended(slot, t1, t1m, w_all) ? slot : sub;
         dma16_asm(base + (size_t)slot * D + (lane % LPR) * 8, lds_addr(stage + dma_dst[k]));
     };
+
+    // the first block's K and V go out before anything else
+#pragma unroll
+    for (int k = 0; k < NIW; ++k) {
+        dma_one(Kh, ks[0], bb_lo, k);
+        dma_one(Vh, vs[0], bb_lo, k);
+    }
+
+    // Q^T operand in AGPRs: Q[column][32 st + 8 grp .. +7]
+    u32x4 qreg[QST];
+    [[maybe_unused]] int b_slot = -1, r_slot = 0;          // the row's own slot, if in this run
+    if constexpr (PREP) {
+        // The workgroup whose run holds the row's slot writes the row's key
+        // and value to the cache for later rows, and to LDS for this one
+        // (copied over the staged slot once its block has landed).  Raw rows
+        // are loaded first; the cos/sin table sits in the second K stage (its
+        // first DMA goes out during block bb_lo's scores).
+        const int slot_t = ring ? p0 % cap : p0;          // p0 >= 0 here (R = 1)
+        const bool owner = slot_t >= slot0 && slot_t < slot0 + nslot && wave < 2;
+        u32x4 kvx[QST];
+        load_row<D>(qreg, pa.qkv + ((size_t)s * (Hq + 2 * Hkv) + h) * D, grp, cv);
+        if (owner) load_kv<D>(kvx, pa, s, g, Hq, Hkv, lane, wave);
+        float* cs = reinterpret_cast<float*>(&ks[1][0]);
+        rope_table<D>(cs, pa.inv_freq, p0, tid, 256);
+        norm_row<D>(qreg, pa.q_w, grp, pa.eps);
+        if (owner) norm_kv<D>(kvx, pa, lane, wave);
+        __syncthreads();
+        rope_row<D>(qreg, cs, grp);
+        if (slot_t >= slot0 && slot_t < slot0 + nslot) {
+            b_slot = (slot_t - slot0) / WKB;
+            r_slot = (slot_t - slot0) % WKB;
+        }
+        if (owner)
+            rope_store_kv<D>(kvx, pa, (((size_t)s * Hkv + g) * cap + slot_t) * D, cs, lane, wave,
+                             kv_new[wave]);
+    } else {
+        const uint16_t* qrow = q + (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * D + 8 * grp;
+#pragma unroll
+        for (int st = 0; st < QST; ++st) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qreg[st] = cv ? ld16(qrow + 32 * st) : z;
+        }
+    }
+#pragma unroll
+    for (int st = 0; st < QST; ++st) asm volatile("" : "+a"(qreg[st]));
 
     const int kofs = row_pos<D, WPAD>(col) + 8 * grp;
     // V^T operand: lane j of a 16-lane group points at the row of k-slot
@@ -321,16 +360,24 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         }
     };
 
-#pragma unroll
-    for (int k = 0; k < NIW; ++k) {
-        dma_one(Kh, ks[0], bb_lo, k);
-        dma_one(Vh, vs[0], bb_lo, k);
-    }
     for (int b = bb_lo; b <= bb_hi; ++b) {
         // block b has landed (every wave's share), and every wave is done
         // with block b - 1's stage
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if constexpr (PREP) {
+            if (b == b_slot) {
+                // the row's own key and value over the staged slot contents
+                const int st = (b - bb_lo) & 1;
+                if (tid < 2 * (D / 8)) {
+                    const int part = tid / (D / 8), piece = tid % (D / 8);
+                    uint16_t* dst = (part ? vs[st] : ks[st]) + row_pos<D, WPAD>(r_slot) + 8 * piece;
+                    *reinterpret_cast<u32x4*>(dst) =
+                        *reinterpret_cast<const u32x4*>(&kv_new[part][8 * piece]);
+                }
+                __syncthreads();
+            }
+        }
         if (b < bb_hi) block(b, (b - bb_lo) & 1, std::true_type{});
         else block(b, (b - bb_lo) & 1, std::false_type{});
     }
@@ -552,7 +599,7 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                          float scale, void* ws, hipStream_t stream) {
     // one row per stream is a window of one row: the same kernel and bits
     return launch_decode_rows(out, q, kc, vc, pos, S, 1, Hq, Hkv, D, cap, ring, window, scale,
-                              ws, false, stream);
+                              ws, false, nullptr, stream);
 }
 
 static hipError_t launch_decode_merge(uint16_t* out, const float* part_acc, const float* part_ml,
@@ -568,7 +615,7 @@ static hipError_t launch_decode_merge(uint16_t* out, const float* part_acc, cons
 hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                               const uint16_t* vc, const int32_t* pos, int S, int R, int Hq,
                               int Hkv, int D, int cap, int ring, int window, float scale,
-                              void* ws, bool fused, hipStream_t stream) {
+                              void* ws, bool fused, const PrepArgs* prep, hipStream_t stream) {
     const int G = Hq / Hkv;
     const int RPT = 16 / G;                      // rows per 16-column tile
     const int NT = (R + RPT - 1) / RPT;          // column tiles of a window
@@ -591,16 +638,19 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
                                                (fused ? ATTN_DECODE_COUNTER_BYTES : 0));
     float* part_ml = part_acc + (size_t)S * R * Hq * nrun * D;
     const float c = scale * ATTN_LOG2E;
-#define ROWS_LAUNCH(DD, SS, FF)                                                               \
-    decode_rows_kernel<DD, SS, FF><<<(unsigned)nwg, 256, 0, stream>>>(                        \
+    const PrepArgs pa = prep ? *prep : PrepArgs{};
+#define ROWS_LAUNCH(DD, SS, FF, PP)                                                           \
+    decode_rows_kernel<DD, SS, FF, PP><<<(unsigned)nwg, 256, 0, stream>>>(                    \
         q, kc, vc, pos, part_acc, part_ml, out, counters, R, Hq, Hkv, G, RPT, NT, CG,         \
-        (int)n_items, cap, nrun, cpr, ring, window, c)
+        (int)n_items, cap, nrun, cpr, ring, window, c, pa)
 #define ROWS_DS(DD, FF)                                                                       \
     do {                                                                                      \
-        if (DS == 4) ROWS_LAUNCH(DD, 4, FF);                                                  \
-        else if (DS == 2) ROWS_LAUNCH(DD, 2, FF);                                             \
-        else ROWS_LAUNCH(DD, 1, FF);                                                          \
+        if (prep) ROWS_LAUNCH(DD, 4, FF, true);                                               \
+        else if (DS == 4) ROWS_LAUNCH(DD, 4, FF, false);                                      \
+        else if (DS == 2) ROWS_LAUNCH(DD, 2, FF, false);                                      \
+        else ROWS_LAUNCH(DD, 1, FF, false);                                                   \
     } while (0)
+    if (prep && R != 1) return hipErrorInvalidValue;       // the prologue serves one row
     if (D == 256) {
         if (one) ROWS_DS(256, true);
         else ROWS_DS(256, false);
@@ -615,14 +665,68 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
     return launch_decode_merge(out, part_acc, part_ml, S * R * Hq, D, nrun, stream);
 }
 
+namespace {
+
 // zero fill of a fused decode's counter area (a kernel, so a graph may hold it)
 __global__ void zero_words_kernel(uint32_t* p, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
 }
 
+}  // namespace
+
 hipError_t launch_decode_counters_init(void* ws, hipStream_t stream) {
     constexpr int n = ATTN_DECODE_COUNTER_BYTES / 4;
     zero_words_kernel<<<(n + 255) / 256, 256, 0, stream>>>(static_cast<uint32_t*>(ws), n);
+    return hipGetLastError();
+}
+
+// Standalone prologue: grid (S, ceil(Hq / 16) + 2 Hkv), one wave each: unit u
+// < ceil(Hq / 16) norms and rotates 16 query heads into q_out; the next Hkv
+// units write the rotated keys, the last Hkv the values, at the row's slot
+// (skipped when the row's position has no slot: t < 0, or t >= cap linear).
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(64)
+void qkv_prep_kernel(uint16_t* __restrict__ q_out, PrepArgs pa, const int32_t* __restrict__ pos,
+                     int Hq, int Hkv, int cap, int ring) {
+    __shared__ float cs[D];
+    const int s = blockIdx.x;
+    const int u = blockIdx.y;
+    const int lane = threadIdx.x;
+    const int col = lane & 15, grp = lane >> 4;
+    const int t = pos[s];
+    const int QT = (Hq + 15) / 16;
+    rope_table<D>(cs, pa.inv_freq, t, lane, 64);
+    __syncthreads();
+    u32x4 x[D / 32];
+    if (u < QT) {
+        const int h = u * 16 + col;
+        const bool ok = h < Hq;
+        load_row<D>(x, pa.qkv + ((size_t)s * (Hq + 2 * Hkv) + (ok ? h : 0)) * D, grp, ok);
+        norm_row<D>(x, pa.q_w, grp, pa.eps);
+        rope_row<D>(x, cs, grp);
+        if (ok) store_row<D>(q_out + ((size_t)s * Hq + h) * D, x, grp);
+        return;
+    }
+    if (t < 0 || (!ring && t >= cap)) return;
+    const int slot = ring ? t % cap : t;
+    const int g = (u - QT) % Hkv;
+    const int part = (u - QT) / Hkv;
+    load_kv<D>(x, pa, s, g, Hq, Hkv, lane, part);
+    norm_kv<D>(x, pa, lane, part);
+    rope_store_kv<D>(x, pa, (((size_t)s * Hkv + g) * cap + slot) * D, cs, lane, part, nullptr);
+}
+
+}  // namespace
+
+hipError_t launch_qkv_prep(uint16_t* q_out, const PrepArgs& pa, const int32_t* pos, int S,
+                           int Hq, int Hkv, int D, int cap, int ring, hipStream_t stream) {
+    const dim3 grid(S, (Hq + 15) / 16 + 2 * Hkv);
+    if (D == 256)
+        qkv_prep_kernel<256><<<grid, 64, 0, stream>>>(q_out, pa, pos, Hq, Hkv, cap, ring);
+    else
+        qkv_prep_kernel<512><<<grid, 64, 0, stream>>>(q_out, pa, pos, Hq, Hkv, cap, ring);
     return hipGetLastError();
 }

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include "../../include/gqa_attn.h"
+#include "prologue.h"
 
 size_t decode_workspace_bytes(int S, int Hq, int D, int cap);
 
@@ -19,10 +20,14 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* kc,
 // q, out [S][R][Hq][D]; ws as decode_workspace_bytes(S * R, Hq, D, cap)
 // fused: one launch where the merge fits a workgroup; ws then starts with
 // ATTN_DECODE_COUNTER_BYTES of counters (zero on entry, left zero)
+// prep (one row per stream, else NULL): queries from the stacked rows,
+// normed and rotated in place; the row's key and value written first
 hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                               const uint16_t* vc, const int32_t* pos, int S, int R, int Hq,
                               int Hkv, int D, int cap, int ring, int window, float scale,
-                              void* ws, bool fused, hipStream_t stream);
+                              void* ws, bool fused, const PrepArgs* prep, hipStream_t stream);
+hipError_t launch_qkv_prep(uint16_t* q_out, const PrepArgs& pa, const int32_t* pos, int S,
+                           int Hq, int Hkv, int D, int cap, int ring, hipStream_t stream);
 hipError_t launch_decode_counters_init(void* ws, hipStream_t stream);
 
 int prefill_key_block(int D, int p_mode);

@@ -213,6 +213,55 @@ int attn_decode_rows_fused(void* out, const void* q, const void* k_cache,
 int attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode prologue of one stacked projection row per stream (PR #1183
+ * squashed commit bodies, the qk_rows note: q and k = bf16(w * bf16(x *
+ * inv)) before the rotary embedding, inv = 1 / sqrt(mean(x^2) + eps), and v
+ * optionally normed by a unit RMS norm; PR #975 decode commits: the row's
+ * key and value go to the cache).  For stream s at t = pos[s], each head's
+ * D values x of q and k are normed with their scale (q_norm_w or k_norm_w,
+ * two bf16 rounding points) and rotated over the head's halves: for
+ * i < D/2, a = fp32(fp32(t) * inv_freq[i]), out_i = bf16(y_i cos a -
+ * y_{i+D/2} sin a), out_{i+D/2} = bf16(y_{i+D/2} cos a + y_i sin a) (cos and
+ * sin of the fp32 angle in fp32; a zero frequency leaves its pair as is).
+ * v is bf16(x * inv) when v_norm = 1, else copied.  q goes to q_out; the
+ * key and value to the cache slot of t (t, or t mod cap in a ring).
+ *
+ *   q_out      device bf16 [S][Hq][D], written
+ *   k_cache    device bf16 [S][Hkv][cap][D], slot of pos[s] written
+ *   v_cache    device bf16 [S][Hkv][cap][D], slot of pos[s] written
+ *   qkv        device bf16 [S][(Hq + 2 Hkv) D]: q heads, k heads, v heads
+ *   q_norm_w   device bf16 [D], 16-byte aligned
+ *   k_norm_w   device bf16 [D], 16-byte aligned
+ *   inv_freq   device fp32 [D/2]
+ *   eps        finite, >= 0 (a zero row with eps = 0 gives NaN)
+ *   v_norm     0 or 1
+ *   pos        device int32 [S]; a row with t < 0, or t >= cap in a linear
+ *              cache, writes no key or value
+ * Errors as attn_decode for shapes; ATTN_E_RANGE for eps or v_norm.
+ */
+int attn_qkv_prep(void* q_out, void* k_cache, void* v_cache, const void* qkv,
+                  const void* q_norm_w, const void* k_norm_w, const float* inv_freq, float eps,
+                  int v_norm, const int32_t* pos, int n_seq, int n_q_heads, int n_kv_heads,
+                  int head_dim, int cache_cap, int ring, void* stream);
+
+/*
+ * attn_qkv_prep followed by attn_decode_rows_fused with one row per stream,
+ * in the decode kernel itself (PR #975 decode commits: the partial kernel
+ * norms and ropes its query heads from the stacked row, the workgroup of
+ * the row's chunk writes the row's key and value to the cache, and with one
+ * chunk it writes the output itself).  Outputs, cache contents and bits are
+ * those of the two calls.  Arguments as the two calls; the caches are
+ * written; the workspace as attn_decode_rows_fused's (counters set up by
+ * attn_decode_workspace_init).
+ */
+int attn_decode_prep_fused(void* out, const void* qkv, const void* q_norm_w,
+                           const void* k_norm_w, const float* inv_freq, float eps, int v_norm,
+                           void* k_cache, void* v_cache, const int32_t* pos, int n_seq,
+                           int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
+                           int ring, int window, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
  * Prompt attention for one stream's chunk of n_rows rows at positions
  * pos0 .. pos0 + n_rows - 1 (PR #975 prompt attention commits; PR #1183
  * window_rows notes).  The chunk's own keys and values must already be in
