@@ -78,6 +78,8 @@ int attn_decode(void* out, const void* q, const void* k_cache,
     if (tensor_bytes(n_seq, n_kv_heads, cache_cap, head_dim) < 0 ||
         tensor_bytes(n_seq, n_q_heads, 1, head_dim) < 0)
         return ATTN_E_RANGE;
+    // one head's cache slice is addressed with 32-bit byte offsets
+    if ((long long)cache_cap * head_dim * 2 >= (1LL << 32)) return ATTN_E_RANGE;
     if (n_seq == 0) return ATTN_OK;
     if (!out || !q || !k_cache || !v_cache || !pos) return ATTN_E_NULL;
     if (!workspace) return ATTN_E_WORKSPACE;
@@ -136,6 +138,8 @@ int decode_rows_call(void* out, const void* q, const void* k_cache, const void* 
     if (tensor_bytes(n_seq, n_kv_heads, cache_cap, head_dim) < 0 ||
         tensor_bytes((long long)n_seq * rows, n_q_heads, 1, head_dim) < 0)
         return ATTN_E_RANGE;
+    // one head's cache slice is addressed with 32-bit byte offsets
+    if ((long long)cache_cap * head_dim * 2 >= (1LL << 32)) return ATTN_E_RANGE;
     // four counters per (stream, KV head) in the fused counter area
     if (fused && (long long)n_seq * n_kv_heads * 4 * 4 > ATTN_DECODE_COUNTER_BYTES)
         return ATTN_E_RANGE;

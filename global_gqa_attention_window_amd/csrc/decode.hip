@@ -195,17 +195,63 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         dma_row[k] = (LPR == 64) ? r0 : r0 + 8 * (lane >> 5);
         dma_dst[k] = row_pos<D, WPAD>(r0);
     }
-    auto dma_one = [&](const uint16_t* base, uint16_t* stage, int b, int k) {
-        int slot = slot0 + b * WKB + dma_row[k];
-        slot = attended(slot, t1, t1m, w_all) ? slot : sub;
-        dma16_asm(base + (size_t)slot * D + (lane % LPR) * 8, lds_addr(stage + dma_dst[k]));
+    // Sources of a block's DMA, as byte offsets (below 2^32) from the head's
+    // K or V base: a block whose 32 slots are all attended by the workgroup's
+    // rows and hold consecutive positions (no ring wrap inside; almost every
+    // block) adds a wave-uniform block offset to per-lane offsets fixed for
+    // the kernel; any other block computes each lane's slot, fetching an
+    // unattended one from the last row's slot instead.
+    uint32_t dma_voff[NIW];
+#pragma unroll
+    for (int k = 0; k < NIW; ++k)
+        dma_voff[k] = (uint32_t)(dma_row[k] * D + (lane % LPR) * 8) * 2u;
+    // (bitwise, without short-circuit branches)
+    auto block_all = [&](int b) -> bool {
+        const int sb = slot0 + b * WKB;
+        const bool wrap = ring & (t1m >= sb) & (t1m < sb + WKB - 1);
+        return (sb + WKB <= cap) & !wrap & attended(sb, t1, t1m, w_all) &
+               attended(sb + WKB - 1, t1, t1m, w_all);
+    };
+    // block b's DMA offsets from the heads' bases Kh, Vh
+    auto dma_plan = [&](int b, uint32_t (&vo)[NIW]) {
+        if (block_all(b)) {
+            const uint32_t boff = (uint32_t)(slot0 + b * WKB) * (uint32_t)D * 2u;
+#pragma unroll
+            for (int k = 0; k < NIW; ++k) vo[k] = boff + dma_voff[k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < NIW; ++k) {
+                int slot = slot0 + b * WKB + dma_row[k];
+                slot = attended(slot, t1, t1m, w_all) ? slot : sub;
+                vo[k] = (uint32_t)(slot * D + (lane % LPR) * 8) * 2u;
+            }
+        }
+    };
+    auto dma_one = [&](const uint16_t* base, uint16_t* stage, const uint32_t (&vo)[NIW], int k) {
+        dma16_asm_sbase(base, vo[k], lds_addr(stage + dma_dst[k]));
+    };
+    // a block every row of the workgroup attends whole needs no mask: all
+    // its slots attended together, its positions (consecutive) within
+    // [last row - W + 1, first row]
+    const int t0r = p0 + r_lo;
+    auto block_nomask = [&](int b) -> bool {
+        const int sb = slot0 + b * WKB;
+        int d = t1m - sb;
+        d += d < 0 ? cap : 0;
+        const int pl = ring ? t1 - d : sb;
+        return block_all(b) && t0r >= 0 && pl + WKB - 1 <= t0r &&
+               (window <= 0 || pl >= t1 - window + 1);
     };
 
     // the first block's K and V go out before anything else
+    {
+        uint32_t vo0[NIW];
+        dma_plan(bb_lo, vo0);
 #pragma unroll
-    for (int k = 0; k < NIW; ++k) {
-        dma_one(Kh, ks[0], bb_lo, k);
-        dma_one(Vh, vs[0], bb_lo, k);
+        for (int k = 0; k < NIW; ++k) {
+            dma_one(Kh, ks[0], vo0, k);
+            dma_one(Vh, vs[0], vo0, k);
+        }
     }
 
     // Q^T operand in AGPRs: Q[column][32 st + 8 grp .. +7]
@@ -259,6 +305,9 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         const uint16_t* kl = ks[st];
         const uint16_t* vl = vs[st];
 
+        uint32_t nvo[NIW];                       // next block's DMA plan
+        if constexpr (MORE) dma_plan(b + 1, nvo);
+        const bool nomask = block_nomask(b);
         u32x4 kb[KPF][2];
 #pragma unroll
         for (int j = 0; j < KPF; ++j) {
@@ -282,8 +331,8 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
                 // they have the whole block to land
 #pragma unroll
                 for (int k = j * 2 * NIW / QST; k < (j + 1) * 2 * NIW / QST; ++k) {
-                    if (k < NIW) dma_one(Kh, ks[st ^ 1], b + 1, k);
-                    else dma_one(Vh, vs[st ^ 1], b + 1, k - NIW);
+                    if (k < NIW) dma_one(Kh, ks[st ^ 1], nvo, k);
+                    else dma_one(Vh, vs[st ^ 1], nvo, k - NIW);
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -301,14 +350,23 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         const int sb = slot0 + b * WKB;
         float tv[8];
         float mx = -INFINITY;
+        if (nomask) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok0 = attended(sb + 4 * grp + i, t_col, tcm, window);
-            const bool ok1 = attended(sb + 16 + 4 * grp + i, t_col, tcm, window);
-            tv[i] = ok0 ? s0[i] * c : -INFINITY;
-            tv[4 + i] = ok1 ? s1[i] * c : -INFINITY;
-            mx = fmaxf(mx, fmaxf(tv[i], tv[4 + i]));
+            for (int i = 0; i < 4; ++i) {
+                tv[i] = s0[i] * c;
+                tv[4 + i] = s1[i] * c;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok0 = attended(sb + 4 * grp + i, t_col, tcm, window);
+                const bool ok1 = attended(sb + 16 + 4 * grp + i, t_col, tcm, window);
+                tv[i] = ok0 ? s0[i] * c : -INFINITY;
+                tv[4 + i] = ok1 ? s1[i] * c : -INFINITY;
+            }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fmaxf(tv[i], tv[4 + i]));
         // reference maximum: moves only when the block maximum passes it by
         // more than 8 (p <= 2^8); a lane that keeps it keeps its bits
         mx = xmax4(mx);

@@ -114,6 +114,8 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_q_heads, int head_dim,
  *   n_seq      S >= 0 (0 launches nothing)
  *   ring       0 linear cache, 1 ring of cap slots
  *   window     W >= 0, 0 = none; a ring needs W <= cap
+ *   cache_cap  cap >= 1, cap * D * 2 < 2^32 (one head's slice in 32-bit byte
+ *              offsets), else ATTN_E_RANGE
  *   scale      finite fp32 score scale
  *   workspace  device, >= attn_decode_workspace_bytes(S, Hq, D, cap) bytes,
  *              16-byte aligned; contents on entry are ignored
