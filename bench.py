@@ -252,7 +252,7 @@ def main():
                    "prompt_tokens": n, "chunk_rows": ch, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": D, "p_mode": "bf16x2", "window": 0,
                    "decode_cache_keys": dcap, "seed": w.seed},
-        "roofline": {"kernel": "prefill_pair_kernel<bf16x2>", "bound": "mfma",
+        "roofline": {"kernel": "prefill_roles_kernel<bf16x2>", "bound": "mfma",
                      "achieved": round(pf_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pf_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
