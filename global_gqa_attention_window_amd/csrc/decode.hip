@@ -565,28 +565,47 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
 }
 
 // Merge of chunk partials in ascending chunk order.  A block of MW waves
-// serves one (stream, head) and 256 d (four per lane); wave w takes the
+// serves one (stream, head) and 64 VEC d (VEC per lane); wave w takes the
 // contiguous chunk range [w nch / MW, (w + 1) nch / MW) in ascending order,
 // then the waves' sums are added in ascending wave order.  M is the largest
 // chunk maximum; chunks with no attended key (m = -inf) are skipped, never
-// multiplied; out = bf16(sum e^(m_c - M) acc_c / sum e^(m_c - M) l_c).
-template <int D>
-__global__ __launch_bounds__(64 * MW)
+// multiplied; out = bf16(sum e^(m_c - M) acc_c / sum e^(m_c - M) l_c), each
+// weighted term added with one rounding (fmaf).  A wave loads MB chunks'
+// partials before it adds them (in order), so that many loads are in flight;
+// the d slice per block (VEC) only spreads the same per-element arithmetic
+// over more blocks.  Registers stay within eight waves per SIMD, so two
+// blocks share a CU.
+template <int D, int VEC>
+__global__ __launch_bounds__(64 * MW) __attribute__((amdgpu_waves_per_eu(8)))
 void decode_merge_kernel(uint16_t* __restrict__ out,
                          const float* __restrict__ part_acc,
                          const float* __restrict__ part_ml,
-                         int Hq, int nch) {
+                         int nch) {
+    constexpr int MB = VEC == 4 ? 4 : 8;     // loads in flight per wave (two blocks a CU)
+    static_assert(VEC == 1 || VEC == 2 || VEC == 4, "lane width");
     __shared__ float s_max[MW];
     __shared__ float s_l[MW];
-    __shared__ f32x4 s_o[MW][64];
+    __shared__ __attribute__((aligned(16))) float s_o[MW][64 * VEC];
     const int sh = blockIdx.x;                 // s * Hq + h
-    const int d0 = blockIdx.y * 256 + (threadIdx.x & 63) * 4;
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    const int d0 = blockIdx.y * (64 * VEC) + lane * VEC;
     const size_t base = (size_t)sh * (size_t)nch;
     const float2* ml = reinterpret_cast<const float2*>(part_ml) + base;
     const int c0 = (int)((long long)w * nch / MW);
     const int c1 = (int)((long long)(w + 1) * nch / MW);
+    auto load = [&](int ci, float (&v)[VEC]) {
+        const float* p = part_acc + (base + ci) * D + d0;
+        if constexpr (VEC == 4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(p);
+            v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+        } else if constexpr (VEC == 2) {
+            const float2 x = *reinterpret_cast<const float2*>(p);
+            v[0] = x.x; v[1] = x.y;
+        } else {
+            v[0] = *p;
+        }
+    };
 
     float mw = -INFINITY;
     for (int cidx = c0 + lane; cidx < c1; cidx += 64) mw = fmaxf(mw, ml[cidx].x);
@@ -599,49 +618,79 @@ void decode_merge_kernel(uint16_t* __restrict__ out,
     for (int i = 0; i < MW; ++i) M = fmaxf(M, s_max[i]);
 
     float L = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-        int cidx = c0;
-        for (; cidx + 4 <= c1; cidx += 4) {
-            f32x4 a[4];
-            float2 e[4];
+    float o[VEC];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                e[u] = ml[cidx + u];
-                a[u] = *reinterpret_cast<const f32x4*>(part_acc + (base + cidx + u) * D + d0);
+    for (int i = 0; i < VEC; ++i) o[i] = 0.f;
+    if (M != -INFINITY) {
+        int cb = c0;
+        for (; cb + MB <= c1; cb += MB) {
+            float2 e[MB];
+            float a[MB][VEC];
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+                e[u] = ml[cb + u];
+                load(cb + u, a[u]);
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < MB; ++u) {
                 if (e[u].x == -INFINITY) continue;
                 const float wt = fast_exp2(e[u].x - M);
-                L += wt * e[u].y;
-                o += wt * a[u];
+                L = fmaf(wt, e[u].y, L);
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) o[i] = fmaf(wt, a[u][i], o[i]);
             }
         }
-        for (; cidx < c1; ++cidx) {
-            const float2 e = ml[cidx];
+        for (; cb < c1; ++cb) {
+            const float2 e = ml[cb];
             if (e.x == -INFINITY) continue;
+            float a[VEC];
+            load(cb, a);
             const float wt = fast_exp2(e.x - M);
-            L += wt * e.y;
-            o += wt * *reinterpret_cast<const f32x4*>(part_acc + (base + cidx) * D + d0);
+            L = fmaf(wt, e.y, L);
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) o[i] = fmaf(wt, a[i], o[i]);
         }
     }
-    s_o[w][lane] = o;
+    float* so = &s_o[w][lane * VEC];
+    if constexpr (VEC == 4) *reinterpret_cast<f32x4*>(so) = f32x4{o[0], o[1], o[2], o[3]};
+    else if constexpr (VEC == 2) *reinterpret_cast<float2*>(so) = float2{o[0], o[1]};
+    else *so = o[0];
     if (lane == 0) s_l[w] = L;
     __syncthreads();
     if (w != 0) return;
     float Lt = 0.f;
-    f32x4 ot = {0.f, 0.f, 0.f, 0.f};
+    float ot[VEC];
 #pragma unroll
-    for (int i = 0; i < MW; ++i) {
-        Lt += s_l[i];
-        ot += s_o[i][lane];
+    for (int i = 0; i < VEC; ++i) ot[i] = 0.f;
+#pragma unroll 4
+    for (int j = 0; j < MW; ++j) {
+        Lt += s_l[j];
+        const float* sj = &s_o[j][lane * VEC];
+        float x[VEC];
+        if constexpr (VEC == 4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sj);
+            x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+        } else if constexpr (VEC == 2) {
+            const float2 v = *reinterpret_cast<const float2*>(sj);
+            x[0] = v.x; x[1] = v.y;
+        } else {
+            x[0] = *sj;
+        }
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) ot[i] += x[i];
     }
-    uint32_t b[4];
+    uint32_t bb[VEC];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = (Lt != 0.f || Lt != Lt) ? f32_to_bf16_bits(ot[i] / Lt) : 0u;
-    u32x2 packed = {pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
-    *reinterpret_cast<u32x2*>(out + (size_t)sh * D + d0) = packed;
+    for (int i = 0; i < VEC; ++i)
+        bb[i] = (Lt != 0.f || Lt != Lt) ? f32_to_bf16_bits(ot[i] / Lt) : 0u;
+    uint16_t* orow = out + (size_t)sh * D + d0;
+    if constexpr (VEC == 4) {
+        *reinterpret_cast<u32x2*>(orow) = u32x2{pack_bf16x2(bb[0], bb[1]), pack_bf16x2(bb[2], bb[3])};
+    } else if constexpr (VEC == 2) {
+        *reinterpret_cast<uint32_t*>(orow) = pack_bf16x2(bb[0], bb[1]);
+    } else {
+        *orow = (uint16_t)bb[0];
+    }
 }
 
 }  // namespace
@@ -662,11 +711,23 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* kc,
 
 static hipError_t launch_decode_merge(uint16_t* out, const float* part_acc, const float* part_ml,
                                int n_rows_heads, int D, int nrun, hipStream_t stream) {
-    const dim3 g2(n_rows_heads, D / 256);
-    if (D == 256)
-        decode_merge_kernel<256><<<g2, 64 * MW, 0, stream>>>(out, part_acc, part_ml, 0, nrun);
-    else
-        decode_merge_kernel<512><<<g2, 64 * MW, 0, stream>>>(out, part_acc, part_ml, 0, nrun);
+    // narrow d slices when few (stream, head) rows carry many runs each, so
+    // the merge still spreads over the chip
+    const long long wide = (long long)n_rows_heads * (D / 256);
+    const int vec = (nrun < 64 || wide >= 512) ? 4 : (2 * wide >= 512 ? 2 : 1);
+    const dim3 g2(n_rows_heads, D / (64 * vec));
+#define MERGE_LAUNCH(DD, VV) \
+    decode_merge_kernel<DD, VV><<<g2, 64 * MW, 0, stream>>>(out, part_acc, part_ml, nrun)
+    if (D == 256) {
+        if (vec == 4) MERGE_LAUNCH(256, 4);
+        else if (vec == 2) MERGE_LAUNCH(256, 2);
+        else MERGE_LAUNCH(256, 1);
+    } else {
+        if (vec == 4) MERGE_LAUNCH(512, 4);
+        else if (vec == 2) MERGE_LAUNCH(512, 2);
+        else MERGE_LAUNCH(512, 1);
+    }
+#undef MERGE_LAUNCH
     return hipGetLastError();
 }
 
