@@ -107,6 +107,15 @@ ATTN_DEV void dma16_asm_sbase(const void* base, uint32_t voff, uint32_t lds_byte
 #endif
 }
 
+// Wait until at most N of this wave's vector memory loads are outstanding
+// (loads complete in issue order for the count), with no wait on LDS or
+// export counters: the N most recent global->LDS loads may stay in flight.
+template <int N>
+ATTN_DEV void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Element offset of row r of a K or V block staged in LDS.  D = 512: rows of
 // 1 KiB, each followed by PADP padding elements.  D = 256: rows r and r + 8
 // of each 16-row group share one 1 KiB unit (the two halves of a DMA

@@ -54,13 +54,14 @@ constexpr int WKB = 32;        // keys per block (one P.V product)
 
 // Chunks per run: a workgroup carries one online softmax over a run of
 // consecutive chunks and leaves one partial for it.  Runs grow with the cache
-// (fewer partials to write and merge) up to four chunks; the length depends
-// on the cache capacity alone, so a row's bits depend neither on the number
-// of streams nor on the window width.
+// (fewer partials to write and merge) up to eight chunks, so that a 262144-key
+// cache over two KV heads takes 256 workgroups, one round on the chip; the
+// length depends on the cache capacity alone, so a row's bits depend neither
+// on the number of streams nor on the window width.
 int decode_run_chunks(int cap) {
     const int nch = (cap + CHUNK - 1) / CHUNK;
-    const int r = nch / 32;
-    return r < 1 ? 1 : (r > 4 ? 4 : r);
+    const int r = nch / 16;
+    return r < 1 ? 1 : (r > 8 ? 8 : r);
 }
 constexpr int WPAD = 16;       // LDS padding elements per row (per row pair at 256)
 
@@ -100,6 +101,11 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     constexpr int KPF = 4;                      // score steps of K reads in flight
     constexpr int VG = DTW < 4 ? DTW : 4;       // d tiles per P.V group
     constexpr int NG = DTW / VG;                // P.V groups
+    // Memory-bound shapes (d split over the waves: one or two column tiles)
+    // run K two blocks ahead of its use; a workgroup of four column tiles is
+    // matrix-bound and moves K and V one block ahead, with no barrier inside
+    // a block
+    constexpr bool K2 = DS >= 2;
     static_assert(NIW * 4 == NI && NG * VG == DTW && QST >= KPF && (2 * NIW) % QST == 0,
                   "shapes");
 
@@ -243,7 +249,10 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
                (window <= 0 || pl >= t1 - window + 1);
     };
 
-    // the first block's K and V go out before anything else
+    // the first block's K and V go out before anything else, then the second
+    // block's K (K runs two blocks ahead of its use, V one; with PREP the
+    // second K stage holds the rotary table until the loop starts, so that
+    // block's K goes out once the table has been read)
     {
         uint32_t vo0[NIW];
         dma_plan(bb_lo, vo0);
@@ -251,6 +260,11 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         for (int k = 0; k < NIW; ++k) {
             dma_one(Kh, ks[0], vo0, k);
             dma_one(Vh, vs[0], vo0, k);
+        }
+        if (K2 && !PREP && bb_lo < bb_hi) {
+            dma_plan(bb_lo + 1, vo0);
+#pragma unroll
+            for (int k = 0; k < NIW; ++k) dma_one(Kh, ks[1], vo0, k);
         }
     }
 
@@ -298,15 +312,20 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     // of the wave's d part
     const int vofs = row_pos<D, WPAD>(4 * grp + (col >> 2)) + 4 * (col & 3) + dp * (D / DS);
 
-    // One block from stage st; with MORE, the next block's K and V move into
-    // the other stage beside the score products.
-    auto block = [&](int b, int st, auto more_c) {
-        constexpr bool MORE = decltype(more_c)::value;
+    // One block from stage st.  With NEXT, block b + 1's V (and its K, unless
+    // K2) moves into the other stage beside the score products; with NEXT2
+    // (K2 only), once every wave has read K(b), block b + 2's K moves into
+    // this K stage beside the softmax and P.V products, so about one and a
+    // half blocks stay in flight.
+    auto block = [&](int b, int st, auto next_c, auto next2_c) {
+        constexpr bool NEXT = decltype(next_c)::value;
+        constexpr bool NEXT2 = decltype(next2_c)::value;
         const uint16_t* kl = ks[st];
         const uint16_t* vl = vs[st];
 
-        uint32_t nvo[NIW];                       // next block's DMA plan
-        if constexpr (MORE) dma_plan(b + 1, nvo);
+        uint32_t nvo[NIW], kvo[NIW];             // DMA plans of V(b + 1), K(b + 2)
+        if constexpr (NEXT) dma_plan(b + 1, nvo);
+        if constexpr (NEXT2) dma_plan(b + 2, kvo);
         const bool nomask = block_nomask(b);
         u32x4 kb[KPF][2];
 #pragma unroll
@@ -326,15 +345,24 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
                 kb[j % KPF][0] = ld16(kl + kofs + 32 * (j + KPF));
                 kb[j % KPF][1] = ld16(kl + K16 + kofs + 32 * (j + KPF));
             }
-            if constexpr (MORE) {
-                // both stages of the next block go out during the scores, so
-                // they have the whole block to land
+            if constexpr (NEXT && K2) {
+#pragma unroll
+                for (int k = j * NIW / QST; k < (j + 1) * NIW / QST; ++k)
+                    dma_one(Vh, vs[st ^ 1], nvo, k);
+            } else if constexpr (NEXT) {
 #pragma unroll
                 for (int k = j * 2 * NIW / QST; k < (j + 1) * 2 * NIW / QST; ++k) {
                     if (k < NIW) dma_one(Kh, ks[st ^ 1], nvo, k);
                     else dma_one(Vh, vs[st ^ 1], nvo, k - NIW);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (NEXT2) {
+            // every wave's K(b) reads are done (their products consumed them)
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < NIW; ++k) dma_one(Kh, ks[st], kvo, k);
             __builtin_amdgcn_sched_barrier(0);
         }
         // first V^T group's reads go out before the softmax
@@ -419,9 +447,11 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     };
 
     for (int b = bb_lo; b <= bb_hi; ++b) {
-        // block b has landed (every wave's share), and every wave is done
-        // with block b - 1's stage
-        __builtin_amdgcn_s_waitcnt(0);
+        // block b has landed (every wave's share; only block b + 1's K, issued
+        // last, may still be in flight), and every wave is done with block
+        // b - 1's V stage
+        if (K2 && b < bb_hi && (!PREP || b > bb_lo)) wait_vmcnt<NIW>();
+        else __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if constexpr (PREP) {
             if (b == b_slot) {
@@ -435,9 +465,18 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
                 }
                 __syncthreads();
             }
+            if (K2 && b == bb_lo && bb_lo < bb_hi) {
+                // the rotary table in the second K stage has been read
+                uint32_t vo1[NIW];
+                dma_plan(bb_lo + 1, vo1);
+#pragma unroll
+                for (int k = 0; k < NIW; ++k) dma_one(Kh, ks[1], vo1, k);
+            }
         }
-        if (b < bb_hi) block(b, (b - bb_lo) & 1, std::true_type{});
-        else block(b, (b - bb_lo) & 1, std::false_type{});
+        const int st = (b - bb_lo) & 1;
+        if (K2 && b + 1 < bb_hi) block(b, st, std::true_type{}, std::bool_constant<K2>{});
+        else if (b < bb_hi) block(b, st, std::true_type{}, std::false_type{});
+        else block(b, st, std::false_type{}, std::false_type{});
     }
     }
 
@@ -571,7 +610,8 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
 // chunk maximum; chunks with no attended key (m = -inf) are skipped, never
 // multiplied; out = bf16(sum e^(m_c - M) acc_c / sum e^(m_c - M) l_c), each
 // weighted term added with one rounding (fmaf).  A wave loads MB chunks'
-// partials before it adds them (in order), so that many loads are in flight;
+// partials before it adds them (in order), so that many loads are in flight,
+// and its first MB go out before M is known (the loads do not depend on it);
 // the d slice per block (VEC) only spreads the same per-element arithmetic
 // over more blocks.  Registers stay within eight waves per SIMD, so two
 // blocks share a CU.
@@ -607,6 +647,24 @@ void decode_merge_kernel(uint16_t* __restrict__ out,
         }
     };
 
+    // the batch at cb: runs past c1 read as empty (m = -inf), never loaded
+    float2 e[MB];
+    float a[MB][VEC];
+    auto fetch = [&](int cb) {
+#pragma unroll
+        for (int u = 0; u < MB; ++u) {
+            if (cb + u < c1) {
+                e[u] = ml[cb + u];
+                load(cb + u, a[u]);
+            } else {
+                e[u] = float2{-INFINITY, 0.f};
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) a[u][i] = 0.f;
+            }
+        }
+    };
+    fetch(c0);
+
     float mw = -INFINITY;
     for (int cidx = c0 + lane; cidx < c1; cidx += 64) mw = fmaxf(mw, ml[cidx].x);
 #pragma unroll
@@ -622,15 +680,8 @@ void decode_merge_kernel(uint16_t* __restrict__ out,
 #pragma unroll
     for (int i = 0; i < VEC; ++i) o[i] = 0.f;
     if (M != -INFINITY) {
-        int cb = c0;
-        for (; cb + MB <= c1; cb += MB) {
-            float2 e[MB];
-            float a[MB][VEC];
-#pragma unroll
-            for (int u = 0; u < MB; ++u) {
-                e[u] = ml[cb + u];
-                load(cb + u, a[u]);
-            }
+        for (int cb = c0; cb < c1; cb += MB) {
+            if (cb != c0) fetch(cb);
 #pragma unroll
             for (int u = 0; u < MB; ++u) {
                 if (e[u].x == -INFINITY) continue;
@@ -639,16 +690,6 @@ void decode_merge_kernel(uint16_t* __restrict__ out,
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) o[i] = fmaf(wt, a[u][i], o[i]);
             }
-        }
-        for (; cb < c1; ++cb) {
-            const float2 e = ml[cb];
-            if (e.x == -INFINITY) continue;
-            float a[VEC];
-            load(cb, a);
-            const float wt = fast_exp2(e.x - M);
-            L = fmaf(wt, e.y, L);
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) o[i] = fmaf(wt, a[i], o[i]);
         }
     }
     float* so = &s_o[w][lane * VEC];

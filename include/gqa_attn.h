@@ -95,7 +95,7 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_q_heads, int head_dim,
  * One decode row per stream (PR #1183 window_rows notes; PR #975 decode
  * attention commits).  For stream s and query head h, with t = pos[s]:
  * keys are the cache slots whose position is attended by a row at t; each
- * run c of consecutive 256-slot chunks (1 to 4 chunks, fixed by cap alone)
+ * run c of consecutive 256-slot chunks (1 to 8 chunks, fixed by cap alone)
  * yields m_c (a reference maximum within 8 of the run's largest score, in
  * log2 units), l_c = sum 2^(s log2(e) - m_c) and acc_c = the same weights
  * times v; runs merge in ascending order over M = max m_c; out =

@@ -45,7 +45,8 @@ def _workspace(ga, S, R, Hq, D, cap):
     (256, 32, 4, 1536, 1, 1024, 16, [4080, 5080, 6080]),      # six runs, 16-row windows
     (512, 32, 2, 256, 0, 0, 1, [255, 100, 0, -1]),            # one run: written in place
     (512, 16, 1, 4096, 0, 700, 5, [4091, 2000]),              # sixteen runs
-    (512, 32, 2, 32768, 0, 0, 16, [32752, 20000]),            # 32 runs: partials + merge
+    (512, 32, 2, 32768, 0, 0, 16, [32752, 20000]),            # sixteen runs of eight chunks
+    (512, 32, 2, 65536, 0, 0, 3, [65535, 30000]),             # 32 runs: partials + merge
     (256, 12, 3, 300, 0, 0, 9, [291, 128, 0]),                # G = 4, ragged chunk
 ])
 def test_fused_equals_two_launch_path(ga, D, Hq, Hkv, cap, ring, window, R, pos):

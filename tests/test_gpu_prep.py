@@ -83,7 +83,8 @@ def test_prep_within_oracle_ranges(ga, D, Hq, Hkv, cap, ring, v_norm, theta, pos
     (256, 32, 4, 1024, 1, 1024, 1, [4095 + 1000 * s for s in range(8)]),   # sliding ring
     (256, 8, 1, 512, 0, 512, 0, [511]),                                    # two runs
     (512, 32, 2, 256, 0, 0, 1, [255, 100, 7]),                             # one run, in place
-    (512, 32, 2, 32768, 0, 0, 1, [32767, 12345]),                          # 32 runs: two launches
+    (512, 32, 2, 32768, 0, 0, 1, [32767, 12345]),                          # 16 runs: last-workgroup merge
+    (512, 32, 2, 65536, 0, 0, 1, [65535, 40000]),                          # 32 runs: two launches
 ])
 def test_prep_fused_equals_prep_then_decode(ga, D, Hq, Hkv, cap, ring, window, v_norm, pos):
     import torch
