@@ -9,9 +9,16 @@ linear cache with the same heads.  Inputs are resident in HBM before timing.
 Prints one JSON line: whole-step tokens/s (prompt tokens + the decode token),
 the prefill kernel against the bf16 matrix-core roofline (duration from HIP
 events recorded on the launch stream around every prefill launch), the decode
-kernels against HBM bandwidth, and the CPU oracle timed on a bounded sample.
-Apart from the step, decode windows (16 rows a stream, 8 streams, 32768 keys)
-are timed against the bf16 matrix-core peak.
+kernels against HBM bandwidth (the call inside the step, right after the
+prompt's matrix-heavy launches, and the same call 20 times back to back), and
+the CPU oracle timed on a bounded sample.
+Apart from the step: the 8192-token sliding-layer prompt (128-row chunks
+through a 1152-slot ring, window 1024, head dim 256, P rounded to bf16) in
+prompt tokens/s against the bf16 matrix-core peak; the one-row decode
+workloads of 512 keys, of 8 streams over a 1024-slot sliding ring and of 8
+streams over 32768 global-layer keys against HBM bandwidth; and decode
+windows (16 rows a stream, 8 streams, 32768 keys) against the bf16
+matrix-core peak.
 """
 from __future__ import annotations
 
@@ -39,7 +46,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=24,
+    ap.add_argument("--cpu-rows", type=int, default=96,
                     help="prompt rows of the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 4 plain device copies of MIB MiB each (the known-size "
@@ -121,6 +128,105 @@ def decode_windows(ga, torch, dev, iters: int = 10):
             "us": round(us, 1), "rows_per_s": round(S * R / (us * 1e-6), 1),
             "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "kv_GB/s": round(kv_bytes / (us * 1e-6) / 1e9, 1)}
+
+
+def prefill_sliding(ga, torch, dev, reps: int = 3):
+    """The 8192-token sliding-layer prompt: 64 chunks of 128 rows, each a
+    cache write into the 1152-slot ring then prompt attention over it.
+    Prompt tokens/s over the summed attention-kernel durations (HIP events
+    on the launch stream around each prefill launch) and over the whole
+    chunk sequence with its cache writes; algorithmic flops 4 D per attended
+    (row, key, query head)."""
+    from synthetic.gen import WORKLOADS
+    w = WORKLOADS["prefill_sliding_8k"]
+    n, ch, Hq, Hkv, D = w.n_rows, w.chunk, w.Hq, w.Hkv, w.D
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    q = torch.randn((n, Hq, D), generator=g, device=dev, dtype=torch.bfloat16)
+    k = torch.randn((n, Hkv, D), generator=g, device=dev, dtype=torch.bfloat16)
+    v = torch.randn((n, Hkv, D), generator=g, device=dev, dtype=torch.bfloat16)
+    kc = torch.zeros((Hkv, w.cap, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    out = torch.empty_like(q)
+    starts = list(range(0, n, ch))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in starts]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def prompt(record: bool):
+        for i, r0 in enumerate(starts):
+            m = min(ch, n - r0)
+            ga.attn_cache_write(kc, vc, k[r0:r0 + m], v[r0:r0 + m], r0, m, Hkv, D, w.cap, w.ring)
+            if record:
+                ev[i][0].record()
+            ga.attn_prefill(out[r0:r0 + m], q[r0:r0 + m], kc, vc, r0, m, Hq, Hkv, D, w.cap,
+                            w.ring, w.window, w.scale, w.p_mode)
+            if record:
+                ev[i][1].record()
+    prompt(False)
+    torch.cuda.synchronize()
+    kern_ms, wall_ms = [], []
+    for _ in range(reps):
+        e0.record()
+        prompt(True)
+        e1.record()
+        torch.cuda.synchronize()
+        kern_ms.append(sum(a.elapsed_time(b) for a, b in ev))
+        wall_ms.append(e0.elapsed_time(e1))
+    kms = sorted(kern_ms)[reps // 2]
+    wms = sorted(wall_ms)[reps // 2]
+    flops = causal_pairs(n, w.window) * Hq * 4 * D
+    tf = flops / (kms * 1e-3) / 1e12
+    return {"workload": w.name, "prompt_tokens": n, "chunk_rows": ch, "ring_slots": w.cap,
+            "window": w.window, "head_dim": D, "q_heads": Hq, "kv_heads": Hkv, "p_mode": "bf16",
+            "kernel_ms": round(kms, 3), "tokens_per_s_kernels": round(n / (kms * 1e-3), 1),
+            "wall_ms_with_cache_writes": round(wms, 3),
+            "tokens_per_s_wall": round(n / (wms * 1e-3), 1),
+            "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "launch_us": round(kms * 1e3 / len(starts), 2)}
+
+
+def decode_configs(ga, torch, dev, iters: int = 20):
+    """One-row decode workloads (512 keys; 8 streams over a 1024-slot sliding
+    ring; 8 streams over 32768 global-layer keys): us per call from HIP
+    events over back-to-back calls, K/V bytes attended once per (stream, KV
+    head) plus q and out.  The two smaller caches stay in the 256 MB
+    last-level cache between calls (warm); the 32768-key one (1 GiB) does not."""
+    from synthetic.gen import WORKLOADS
+    res = {}
+    for name in ("decode_g8_d256_512", "decode_sliding_ring1024", "decode_global_32k"):
+        w = WORKLOADS[name]
+        g = torch.Generator(device=dev).manual_seed(w.seed)
+        q = torch.randn((w.S, w.Hq, w.D), generator=g, device=dev, dtype=torch.bfloat16)
+        kc = torch.randn((w.S, w.Hkv, w.cap, w.D), generator=g, device=dev, dtype=torch.bfloat16)
+        vc = torch.randn((w.S, w.Hkv, w.cap, w.D), generator=g, device=dev, dtype=torch.bfloat16)
+        pos = torch.tensor(w.pos, dtype=torch.int32, device=dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(ga.attn_decode_workspace_bytes(w.S, w.Hq, w.D, w.cap),
+                         dtype=torch.uint8, device=dev)
+
+        def call():
+            ga.attn_decode(out, q, kc, vc, pos, w.S, w.Hq, w.Hkv, w.D, w.cap, w.ring, w.window,
+                           w.scale, ws)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        keys = sum(min(w.cap, p + 1) if w.window <= 0 else min(w.cap, p + 1, w.window)
+                   for p in w.pos)
+        nbytes = 2 * w.Hkv * keys * w.D * 2 + 2 * w.S * w.Hq * w.D * 2
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
+                     "cache": "warm" if nbytes < (256 << 20) else "cold"}
+        del q, kc, vc, out, ws
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(q, k, v, w, n_rows_sample: int):
@@ -263,8 +369,25 @@ def main():
         "decode": {"us": round(dec_us, 2), "GB/s": round(dec_gbs, 1),
                    "frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4), "bytes": dec_bytes},
     }
+    # the same decode call 20 times back to back (its 1 GiB K/V still comes
+    # from HBM each time: it is four times the last-level cache)
+    for _ in range(3):
+        ga.attn_decode(dout, dq, dk, dv, dpos_t, 1, Hq, Hkv, D, dcap, 0, 0, w.scale, ws)
+    torch.cuda.synchronize()
+    ev_dec[0].record()
+    for _ in range(20):
+        ga.attn_decode(dout, dq, dk, dv, dpos_t, 1, Hq, Hkv, D, dcap, 0, 0, w.scale, ws)
+    ev_dec[1].record()
+    torch.cuda.synchronize()
+    rep_us = ev_dec[0].elapsed_time(ev_dec[1]) * 1e3 / 20
+    rep_gbs = dec_bytes / (rep_us * 1e-6) / 1e9
+    rec["decode"].update({"us_back_to_back": round(rep_us, 2),
+                          "GB/s_back_to_back": round(rep_gbs, 1),
+                          "frac_hbm_back_to_back": round(rep_gbs / PEAK_HBM_GBS, 4)})
     del q, k, v, kc, vc, out, dk, dv
     torch.cuda.empty_cache()
+    rec["prefill_sliding_8k"] = prefill_sliding(ga, torch, dev)
+    rec["decode_configs"] = decode_configs(ga, torch, dev)
     rec["decode_windows"] = decode_windows(ga, torch, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, w, args.cpu_rows)

@@ -507,9 +507,10 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     for (int b = b_lo; b < b_hi; ++b) {
         const int st = (b - b_lo) & 1;
         // in LDS now: V(b) in vs[st], K(b + 1) in ks[st ^ 1]; P(b) in pch / pcl.
-        // K(b + 2) goes to ks[st] and V(b + 1) to vs[st ^ 1], one instruction
-        // every DMA_EVERY steps (past b_hi the K stage takes filler rows that
-        // nothing reads).
+        // K(b + 2) goes to ks[st] and V(b + 1) to vs[st ^ 1] beside the score
+        // products, one instruction of each every DMA_EVERY steps, so both
+        // have the whole P.V phase to land before the iteration's wait (past
+        // b_hi the K stage takes filler rows that nothing reads).
         l2_prefetch(b + PF_AHEAD);
         const uint16_t *kbase, *vbase;
         uint32_t kvoff[IPW], vvoff[IPW], klds, vlds;
@@ -518,11 +519,10 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         auto k_hook = [&](int j) {
             if (j % DMA_EVERY == 0 && j / DMA_EVERY < IPW)
                 dma_issue(kbase, kvoff, klds, lane_dst, j / DMA_EVERY);
-        };
-        auto v_hook = [&](int j) {
-            if (j % DMA_EVERY == 0 && j / DMA_EVERY < IPW)
+            if (j % DMA_EVERY == DMA_EVERY / 2 && j / DMA_EVERY < IPW)
                 dma_issue(vbase, vvoff, vlds, lane_dstv, j / DMA_EVERY);
         };
+        auto v_hook = [](int) {};
         if (head_ok) {
             f32x4 sacc[KT];
             score_phase(ks_lds[st ^ 1], vs_lds[st], sacc, vb, sm_alpha, k_hook);
