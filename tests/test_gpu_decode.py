@@ -62,6 +62,12 @@ def test_decode_262144_keys(ga):
     (512, 16, 1, 520, 1, 333, [519, 1000, 33, 5]),
     (256, 12, 3, 300, 0, 0, [299, 128, 0]),                              # G = 4
     (512, 2, 2, 256, 0, 0, [255, 100]),                                  # G = 1
+    # runs of five chunks (86 chunks: 17 full runs, a one-chunk run of 240
+    # slots), rows whose last key falls at run and chunk boundaries
+    (512, 32, 2, 22000, 0, 0, [21999, 6399, 6400, 12799, 1279, 1280, 255, 0]),
+    # runs of seven chunks on a ring (118 chunks, the last one partial), wraps
+    # and windows that start and end inside runs
+    (256, 16, 2, 30000, 1, 30000, [29999, 31000, 64000, 1791, 1792, 45000]),
 ])
 def test_decode_ragged_shapes(ga, D, Hq, Hkv, cap, ring, window, pos):
     say("decode ragged", D, Hq, Hkv, cap, ring, window, pos)

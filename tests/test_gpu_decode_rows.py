@@ -57,6 +57,7 @@ def test_decode_rows_global_32k_sampled_streams(ga):
     (512, 2, 2, 256, 0, 0, 16, [240, 100]),                     # G = 1: one tile of 16 rows
     (256, 6, 2, 200, 1, 50, 13, [400, 62]),                     # G = 3, ring of W + R - 1
     (256, 8, 1, 512, 0, 512, 1, [511]),                         # one row
+    (512, 32, 2, 24576, 0, 5000, 6, [24570, 1530, 9000]),      # runs of six chunks, window
 ])
 def test_decode_rows_shapes(ga, D, Hq, Hkv, cap, ring, window, R, pos):
     say("decode rows shape", D, Hq, Hkv, cap, ring, window, R, pos)
