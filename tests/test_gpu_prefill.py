@@ -78,6 +78,8 @@ def test_prefill_global_32k_full(ga):
     (256, 6, 2, 0, 200, 5, 16, 100, 0, P_BF16),             # G = 3, tiny window
     (256, 2, 2, 1, 64, 1, 16, 130, 0, P_BF16X2),            # G = 1, window of 1
     (512, 16, 1, 1, 96, 33, 64, 200, 0, P_BF16),            # ring < block span
+    (256, 8, 1, 0, 64, 0, 1, 20, 0, P_BF16),                # one-row chunks (decode-like)
+    (512, 16, 1, 1, 40, 8, 1, 45, 3, P_BF16X2),             # one-row chunks through a ring
 ])
 def test_prefill_shapes(ga, D, Hq, Hkv, ring, cap, window, chunk, n, pos0, p_mode):
     say("prefill shape", D, Hq, Hkv, ring, cap, window, chunk, n, pos0, p_mode)
@@ -156,3 +158,20 @@ def test_prefill_bits_independent_of_chunking(ga, D, p_mode):
             for ch in (512, 128, 48, 512)]
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
+
+
+def test_prefill_empty_chunk_leaves_output(ga):
+    """A chunk of zero rows is accepted and writes nothing."""
+    import torch
+    from gpu_util import DEV
+    say("prefill empty chunk")
+    for D, p_mode in ((256, P_BF16), (512, P_BF16X2)):
+        kc = torch.zeros((1, 64, D), dtype=torch.int16, device=DEV)
+        vc = torch.zeros_like(kc)
+        out = torch.full((4, 8, D), 0x1234, dtype=torch.int16, device=DEV)
+        q = torch.zeros((4, 8, D), dtype=torch.int16, device=DEV)
+        ga.attn_cache_write(kc, vc, q[:0, :1], q[:0, :1], 10, 0, 1, D, 64, 0)
+        ga.attn_prefill(out, q, kc, vc, 10, 0, 8, 1, D, 64, 0, 0, 0.05, p_mode)
+        torch.cuda.synchronize()
+        assert int((out != 0x1234).sum()) == 0
+        assert int(kc.count_nonzero()) == 0
