@@ -16,9 +16,11 @@ Apart from the step: the 8192-token sliding-layer prompt (128-row chunks
 through a 1152-slot ring, window 1024, head dim 256, P rounded to bf16) in
 prompt tokens/s against the bf16 matrix-core peak; the one-row decode
 workloads of 512 keys, of 8 streams over a 1024-slot sliding ring and of 8
-streams over 32768 global-layer keys against HBM bandwidth; and decode
-windows (16 rows a stream, 8 streams, 32768 keys) against the bf16
-matrix-core peak.
+streams over 32768 global-layer keys against HBM bandwidth (the two small
+ones also cold, rotating over K/V sets larger than the last-level cache);
+decode windows (16 rows a stream, 8 streams, 32768 keys) against the bf16
+matrix-core peak; and the attainable copy bandwidth and bf16 matrix-product
+rate of library kernels on the part, beside the published peaks.
 """
 from __future__ import annotations
 
@@ -229,6 +231,88 @@ def decode_configs(ga, torch, dev, iters: int = 20):
     return res
 
 
+def decode_cold(ga, torch, dev, min_bytes: int = 600 << 20):
+    """The two small one-row decode workloads with their K/V out of the
+    last-level cache: calls rotate over distinct K/V sets totalling more than
+    600 MB (over twice the 256 MB cache), so every call's K/V comes from
+    HBM; us per call (HIP events over one pass of the rotation)."""
+    from synthetic.gen import WORKLOADS
+    res = {}
+    for name in ("decode_g8_d256_512", "decode_sliding_ring1024"):
+        w = WORKLOADS[name]
+        per_set = 2 * w.S * w.Hkv * w.cap * w.D * 2
+        n_sets = max(16, -(-min_bytes // per_set))
+        g = torch.Generator(device=dev).manual_seed(w.seed)
+        q = torch.randn((w.S, w.Hq, w.D), generator=g, device=dev, dtype=torch.bfloat16)
+        kv = torch.randn((n_sets, 2, w.S, w.Hkv, w.cap, w.D), generator=g, device=dev,
+                         dtype=torch.bfloat16)
+        pos = torch.tensor(w.pos, dtype=torch.int32, device=dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(ga.attn_decode_workspace_bytes(w.S, w.Hq, w.D, w.cap),
+                         dtype=torch.uint8, device=dev)
+
+        def call(i):
+            ga.attn_decode(out, q, kv[i, 0], kv[i, 1], pos, w.S, w.Hq, w.Hkv, w.D, w.cap,
+                           w.ring, w.window, w.scale, ws)
+        for i in range(n_sets):
+            call(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_sets):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n_sets
+        keys = sum(min(w.cap, p + 1, w.window) for p in w.pos)
+        nbytes = 2 * w.Hkv * keys * w.D * 2 + 2 * w.S * w.Hq * w.D * 2
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 2), "GB/s": round(gbs, 1),
+                     "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "kv_sets": n_sets,
+                     "rotated_MB": round(n_sets * per_set / 1e6, 1)}
+        del q, kv, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def attainable(torch, dev):
+    """Attainable rates on this part with library kernels, beside the
+    published peaks: a 1 GiB device-to-device copy (bytes read + written per
+    second) and an 8192 x 8192 x 8192 bf16 matrix product (torch.matmul,
+    contiguous operands)."""
+    n = 1 << 29
+    a = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 2 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    m = 8192
+    x = torch.randn((m, m), device=dev, dtype=torch.bfloat16)
+    y = torch.randn((m, m), device=dev, dtype=torch.bfloat16)
+    for _ in range(2):
+        z = torch.matmul(x, y)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        z = torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    mm_tf = 2 * m ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"copy_GB/s": round(copy_gbs, 1), "copy_frac_hbm_peak": round(copy_gbs / PEAK_HBM_GBS, 4),
+            "bf16_gemm_TFLOP/s": round(mm_tf, 1),
+            "bf16_gemm_frac_peak": round(mm_tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def cpu_baseline(q, k, v, w, n_rows_sample: int):
     """The oracle as it stands, on prompt rows spread evenly over the prompt
     (per-row cost grows with position, so an even spread has the prompt's
@@ -388,7 +472,9 @@ def main():
     torch.cuda.empty_cache()
     rec["prefill_sliding_8k"] = prefill_sliding(ga, torch, dev)
     rec["decode_configs"] = decode_configs(ga, torch, dev)
+    rec["decode_configs_cold"] = decode_cold(ga, torch, dev)
     rec["decode_windows"] = decode_windows(ga, torch, dev)
+    rec["attainable"] = attainable(torch, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, w, args.cpu_rows)
     print(json.dumps(rec), flush=True)
