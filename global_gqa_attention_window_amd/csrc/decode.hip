@@ -103,9 +103,10 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     constexpr int NG = DTW / VG;                // P.V groups
     // Memory-bound shapes (d split over the waves: one or two column tiles)
     // run K two blocks ahead of its use; a workgroup of four column tiles is
-    // matrix-bound and moves K and V one block ahead, with no barrier inside
-    // a block
-    constexpr bool K2 = DS >= 2;
+    // matrix-bound, and the single-launch form serves short runs where the
+    // barrier inside each block costs more than the deeper prefetch gains:
+    // those move K and V one block ahead, with no barrier inside a block
+    constexpr bool K2 = DS >= 2 && !FUSE;
     static_assert(NIW * 4 == NI && NG * VG == DTW && QST >= KPF && (2 * NIW) % QST == 0,
                   "shapes");
 
