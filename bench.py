@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=96,
+    ap.add_argument("--cpu-rows", type=int, default=128,
                     help="prompt rows of the oracle's timed sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 4 plain device copies of MIB MiB each (the known-size "
