@@ -112,7 +112,7 @@ size_t attn_decode_rows_workspace_bytes(int n_seq, int rows, int n_q_heads, int 
 namespace {
 
 // checks of the prologue's own arguments (stacked rows, scales, frequencies)
-int check_prep(const PrepArgs& pa) {
+static int check_prep(const PrepArgs& pa) {
     if (!pa.qkv || !pa.q_w || !pa.k_w || !pa.inv_freq) return ATTN_E_NULL;
     if (!aligned16(pa.qkv) || !aligned16(pa.q_w) || !aligned16(pa.k_w) ||
         (reinterpret_cast<uintptr_t>(pa.inv_freq) & 3u) != 0)
@@ -122,7 +122,7 @@ int check_prep(const PrepArgs& pa) {
     return ATTN_OK;
 }
 
-int decode_rows_call(void* out, const void* q, const void* k_cache, const void* v_cache,
+static int decode_rows_call(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* pos, int n_seq, int rows, int n_q_heads, int n_kv_heads,
                      int head_dim, int cache_cap, int ring, int window, float scale,
                      void* workspace, size_t workspace_bytes, bool fused,
@@ -247,11 +247,12 @@ int attn_prefill_key_block(int head_dim, int p_mode) {
     return prefill_key_block(head_dim, p_mode);
 }
 
-int attn_prefill(void* out, const void* q, const void* k_cache,
-                 const void* v_cache, int pos0, int n_rows, int n_q_heads,
-                 int n_kv_heads, int head_dim, int cache_cap, int ring,
-                 int window, float scale, int p_mode,
-                 const int32_t* last_key, void* stream) {
+namespace {
+
+// Argument checks of attn_prefill, up to (not including) the n_rows == 0
+// early return and the pointer checks.
+static int check_prefill(int pos0, int n_rows, int n_q_heads, int n_kv_heads, int head_dim,
+                  int cache_cap, int ring, int window, float scale, int p_mode) {
     int st = check_heads(n_q_heads, n_kv_heads, head_dim);
     if (st != ATTN_OK) return st;
     if (p_mode != ATTN_P_BF16 && p_mode != ATTN_P_BF16X2) return ATTN_E_P_MODE;
@@ -268,6 +269,21 @@ int attn_prefill(void* out, const void* q, const void* k_cache,
     if (tensor_bytes(1, n_kv_heads, cache_cap, head_dim) < 0 ||
         tensor_bytes(n_rows, n_q_heads, 1, head_dim) < 0)
         return ATTN_E_RANGE;
+    // one head's cache slice is addressed with 32-bit byte offsets
+    if ((long long)cache_cap * head_dim * 2 >= (1LL << 32)) return ATTN_E_RANGE;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+int attn_prefill(void* out, const void* q, const void* k_cache,
+                 const void* v_cache, int pos0, int n_rows, int n_q_heads,
+                 int n_kv_heads, int head_dim, int cache_cap, int ring,
+                 int window, float scale, int p_mode,
+                 const int32_t* last_key, void* stream) {
+    const int st = check_prefill(pos0, n_rows, n_q_heads, n_kv_heads, head_dim, cache_cap,
+                                 ring, window, scale, p_mode);
+    if (st != ATTN_OK) return st;
     if (n_rows == 0) return ATTN_OK;
     if (!out || !q || !k_cache || !v_cache) return ATTN_E_NULL;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))

@@ -283,6 +283,8 @@ int attn_decode_prep_fused(void* out, const void* qkv, const void* q_norm_w,
  *   n_rows    >= 0 (0 launches nothing)
  *   ring      0 linear (pos0 + n_rows <= cap), 1 ring (0 < W <= cap and
  *             cap >= W + n_rows - 1, so no row's keys are overwritten)
+ *   cache_cap cap * D * 2 < 2^32 (one head's slice in 32-bit byte offsets),
+ *             else ATTN_E_RANGE
  *   p_mode    ATTN_P_BF16 or ATTN_P_BF16X2
  *   last_key  NULL: each row's last key is its own position (causal).  Or
  *             device int32 [n_rows], 4-byte aligned: the last key position

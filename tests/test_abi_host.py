@@ -147,6 +147,12 @@ def test_prefill_refusals(ga, kw, status):
     assert _prefill(ga, **kw) == _status(status)
 
 
+def test_prefill_refuses_slices_past_32_bit_offsets(ga):
+    # one head's cache slice is addressed with 32-bit byte offsets
+    assert _prefill(ga, ring=0, window=0, D=512, cap=1 << 22, n=0) == _status("ATTN_E_RANGE")
+    assert _prefill(ga, ring=0, window=0, D=512, cap=(1 << 22) - 1, n=0) == 0
+
+
 def test_prefill_edges_accepted_by_checks(ga):
     # exact fits pass the checks; n = 0 returns before any launch
     assert _prefill(ga, n=0, out=None) == 0
