@@ -7,7 +7,10 @@ the attention runs in the library's gfx950 kernels; there is no fallback.  If
 the library has not been built, importing this package raises ImportError.
 
 PyTorch is used for device memory and streams only.  bf16 tensors may be
-torch.bfloat16 or 16-bit integer tensors holding bf16 bit patterns.
+torch.bfloat16 or 16-bit integer tensors holding bf16 bit patterns.  Before
+each call the binding checks that every tensor it passes is contiguous, on
+the current GPU, of the element size the call takes and at least as large as
+the sizes given (the C ABI receives bare pointers and cannot check sizes).
 """
 from __future__ import annotations
 
@@ -71,12 +74,40 @@ def library_path() -> str:
     return _LIB_PATH
 
 
-def _ptr(t):
+def _arg(t, name: str, numel: int, esize: int = 2):
+    """Data pointer of a tensor on the current GPU that holds at least
+    `numel` contiguous elements of `esize` bytes, checked here because the C
+    ABI receives bare pointers and cannot.  None passes through as NULL (the
+    library refuses it where the call needs the buffer)."""
     if t is None:
         return None
-    if isinstance(t, int):
-        return t
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if t.device.type != "cuda" or t.get_device() != torch.cuda.current_device():
+        raise ValueError(f"{name}: on {t.device}, not the current GPU")
+    if t.element_size() != esize:
+        raise ValueError(f"{name}: {t.dtype} has {t.element_size()}-byte elements, "
+                         f"expected {esize}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: not contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, the sizes given need {numel}")
     return t.data_ptr()
+
+
+def _ws(workspace, workspace_bytes):
+    """Pointer and byte count of a workspace tensor; an explicit byte count
+    may not exceed the tensor."""
+    if workspace is None:
+        return None, int(workspace_bytes or 0)
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError(f"workspace: expected a torch.Tensor, got {type(workspace).__name__}")
+    have = workspace.numel() * workspace.element_size()
+    if workspace_bytes is None:
+        workspace_bytes = have
+    if workspace_bytes > have:
+        raise ValueError(f"workspace: {have} bytes, workspace_bytes says {workspace_bytes}")
+    return _arg(workspace, "workspace", 0, workspace.element_size()), int(workspace_bytes)
 
 
 def _stream(stream):
@@ -116,12 +147,12 @@ def attn_decode(out, q, k_cache, v_cache, pos, n_seq, n_q_heads, n_kv_heads,
                 head_dim, cache_cap, ring, window, scale, workspace,
                 workspace_bytes=None, stream=None) -> None:
     """out/q [S][Hq][D], caches [S][Hkv][cap][D] (bf16), pos int32 [S]."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
-    st = _lib.attn_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pos),
+    nq, nc = n_seq * n_q_heads * head_dim, n_seq * n_kv_heads * cache_cap * head_dim
+    wp, wb = _ws(workspace, workspace_bytes)
+    st = _lib.attn_decode(_arg(out, "out", nq), _arg(q, "q", nq), _arg(k_cache, "k_cache", nc),
+                          _arg(v_cache, "v_cache", nc), _arg(pos, "pos", n_seq, 4),
                           n_seq, n_q_heads, n_kv_heads, head_dim, cache_cap, ring,
-                          window, float(scale), _ptr(workspace), int(workspace_bytes),
-                          _stream(stream))
+                          window, float(scale), wp, wb, _stream(stream))
     _ok(st, "attn_decode")
 
 
@@ -130,11 +161,12 @@ def attn_decode_rows(out, q, k_cache, v_cache, pos, n_seq, rows, n_q_heads, n_kv
                      workspace_bytes=None, stream=None) -> None:
     """out/q [S][rows][Hq][D], caches [S][Hkv][cap][D] (bf16), pos int32 [S]
     (the first row's position)."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
-    st = _lib.attn_decode_rows(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pos),
-                               n_seq, rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring,
-                               window, float(scale), _ptr(workspace), int(workspace_bytes),
+    nq, nc = n_seq * rows * n_q_heads * head_dim, n_seq * n_kv_heads * cache_cap * head_dim
+    wp, wb = _ws(workspace, workspace_bytes)
+    st = _lib.attn_decode_rows(_arg(out, "out", nq), _arg(q, "q", nq),
+                               _arg(k_cache, "k_cache", nc), _arg(v_cache, "v_cache", nc),
+                               _arg(pos, "pos", n_seq, 4), n_seq, rows, n_q_heads, n_kv_heads,
+                               head_dim, cache_cap, ring, window, float(scale), wp, wb,
                                _stream(stream))
     _ok(st, "attn_decode_rows")
 
@@ -144,12 +176,13 @@ def attn_decode_rows_fused(out, q, k_cache, v_cache, pos, n_seq, rows, n_q_heads
                            workspace_bytes=None, stream=None) -> None:
     """attn_decode_rows in one launch where it can; the workspace starts with
     ATTN_DECODE_COUNTER_BYTES of counters set up by attn_decode_workspace_init."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
-    st = _lib.attn_decode_rows_fused(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                                     _ptr(pos), n_seq, rows, n_q_heads, n_kv_heads, head_dim,
-                                     cache_cap, ring, window, float(scale), _ptr(workspace),
-                                     int(workspace_bytes), _stream(stream))
+    nq, nc = n_seq * rows * n_q_heads * head_dim, n_seq * n_kv_heads * cache_cap * head_dim
+    wp, wb = _ws(workspace, workspace_bytes)
+    st = _lib.attn_decode_rows_fused(_arg(out, "out", nq), _arg(q, "q", nq),
+                                     _arg(k_cache, "k_cache", nc), _arg(v_cache, "v_cache", nc),
+                                     _arg(pos, "pos", n_seq, 4), n_seq, rows, n_q_heads,
+                                     n_kv_heads, head_dim, cache_cap, ring, window,
+                                     float(scale), wp, wb, _stream(stream))
     _ok(st, "attn_decode_rows_fused")
 
 
@@ -158,10 +191,15 @@ def attn_qkv_prep(q_out, k_cache, v_cache, qkv, q_norm_w, k_norm_w, inv_freq, ep
                   stream=None) -> None:
     """qkv [S][(Hq + 2 Hkv) D] bf16 -> q_out [S][Hq][D], key/value at each
     row's cache slot; inv_freq fp32 [D/2]."""
-    st = _lib.attn_qkv_prep(_ptr(q_out), _ptr(k_cache), _ptr(v_cache), _ptr(qkv),
-                            _ptr(q_norm_w), _ptr(k_norm_w), _ptr(inv_freq), float(eps),
-                            int(v_norm), _ptr(pos), n_seq, n_q_heads, n_kv_heads, head_dim,
-                            cache_cap, ring, _stream(stream))
+    nq, nc = n_seq * n_q_heads * head_dim, n_seq * n_kv_heads * cache_cap * head_dim
+    nx = n_seq * (n_q_heads + 2 * n_kv_heads) * head_dim
+    st = _lib.attn_qkv_prep(_arg(q_out, "q_out", nq), _arg(k_cache, "k_cache", nc),
+                            _arg(v_cache, "v_cache", nc), _arg(qkv, "qkv", nx),
+                            _arg(q_norm_w, "q_norm_w", head_dim),
+                            _arg(k_norm_w, "k_norm_w", head_dim),
+                            _arg(inv_freq, "inv_freq", head_dim // 2, 4), float(eps),
+                            int(v_norm), _arg(pos, "pos", n_seq, 4), n_seq, n_q_heads,
+                            n_kv_heads, head_dim, cache_cap, ring, _stream(stream))
     _ok(st, "attn_qkv_prep")
 
 
@@ -170,21 +208,23 @@ def attn_decode_prep_fused(out, qkv, q_norm_w, k_norm_w, inv_freq, eps, v_norm, 
                            ring, window, scale, workspace, workspace_bytes=None,
                            stream=None) -> None:
     """attn_qkv_prep + one-row attn_decode_rows_fused in the decode kernel."""
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
-    st = _lib.attn_decode_prep_fused(_ptr(out), _ptr(qkv), _ptr(q_norm_w), _ptr(k_norm_w),
-                                     _ptr(inv_freq), float(eps), int(v_norm), _ptr(k_cache),
-                                     _ptr(v_cache), _ptr(pos), n_seq, n_q_heads, n_kv_heads,
-                                     head_dim, cache_cap, ring, window, float(scale),
-                                     _ptr(workspace), int(workspace_bytes), _stream(stream))
+    nq, nc = n_seq * n_q_heads * head_dim, n_seq * n_kv_heads * cache_cap * head_dim
+    nx = n_seq * (n_q_heads + 2 * n_kv_heads) * head_dim
+    wp, wb = _ws(workspace, workspace_bytes)
+    st = _lib.attn_decode_prep_fused(_arg(out, "out", nq), _arg(qkv, "qkv", nx),
+                                     _arg(q_norm_w, "q_norm_w", head_dim),
+                                     _arg(k_norm_w, "k_norm_w", head_dim),
+                                     _arg(inv_freq, "inv_freq", head_dim // 2, 4), float(eps),
+                                     int(v_norm), _arg(k_cache, "k_cache", nc),
+                                     _arg(v_cache, "v_cache", nc), _arg(pos, "pos", n_seq, 4),
+                                     n_seq, n_q_heads, n_kv_heads, head_dim, cache_cap, ring,
+                                     window, float(scale), wp, wb, _stream(stream))
     _ok(st, "attn_decode_prep_fused")
 
 
 def attn_decode_workspace_init(workspace, workspace_bytes=None, stream=None) -> None:
-    if workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
-    _ok(_lib.attn_decode_workspace_init(_ptr(workspace), int(workspace_bytes), _stream(stream)),
-        "attn_decode_workspace_init")
+    wp, wb = _ws(workspace, workspace_bytes)
+    _ok(_lib.attn_decode_workspace_init(wp, wb, _stream(stream)), "attn_decode_workspace_init")
 
 
 def attn_prefill(out, q, k_cache, v_cache, pos0, n_rows, n_q_heads, n_kv_heads,
@@ -192,16 +232,19 @@ def attn_prefill(out, q, k_cache, v_cache, pos0, n_rows, n_q_heads, n_kv_heads,
                  last_key=None, stream=None) -> None:
     """out/q [n_rows][Hq][D], caches [Hkv][cap][D] (bf16); last_key: None
     (causal) or a device int32 [n_rows] of each row's last key position."""
-    st = _lib.attn_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), pos0,
-                           n_rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring,
-                           window, float(scale), p_mode, _ptr(last_key), _stream(stream))
+    nq, nc = n_rows * n_q_heads * head_dim, n_kv_heads * cache_cap * head_dim
+    st = _lib.attn_prefill(_arg(out, "out", nq), _arg(q, "q", nq), _arg(k_cache, "k_cache", nc),
+                           _arg(v_cache, "v_cache", nc), pos0, n_rows, n_q_heads, n_kv_heads,
+                           head_dim, cache_cap, ring, window, float(scale), p_mode,
+                           _arg(last_key, "last_key", n_rows, 4), _stream(stream))
     _ok(st, "attn_prefill")
 
 
 def attn_cache_write(k_cache, v_cache, k, v, pos0, n_rows, n_kv_heads, head_dim,
                      cache_cap, ring, stream=None) -> None:
     """k/v [n_rows][Hkv][D] into caches [Hkv][cap][D] (bf16)."""
-    st = _lib.attn_cache_write(_ptr(k_cache), _ptr(v_cache), _ptr(k), _ptr(v), pos0,
-                               n_rows, n_kv_heads, head_dim, cache_cap, ring,
-                               _stream(stream))
+    nc, nk = n_kv_heads * cache_cap * head_dim, n_rows * n_kv_heads * head_dim
+    st = _lib.attn_cache_write(_arg(k_cache, "k_cache", nc), _arg(v_cache, "v_cache", nc),
+                               _arg(k, "k", nk), _arg(v, "v", nk), pos0, n_rows, n_kv_heads,
+                               head_dim, cache_cap, ring, _stream(stream))
     _ok(st, "attn_cache_write")

@@ -65,11 +65,14 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_q_heads, int head_dim,
     return decode_workspace_bytes(n_seq, n_q_heads, head_dim, cache_cap);
 }
 
-int attn_decode(void* out, const void* q, const void* k_cache,
-                const void* v_cache, const int32_t* pos, int n_seq,
-                int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
-                int ring, int window, float scale, void* workspace,
-                size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// Checks of attn_decode's arguments other than its workspace, in the order
+// the call makes them; ATTN_OK with n_seq == 0 means "nothing to launch".
+int decode_args_status(const void* out, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* pos, int n_seq, int n_q_heads,
+                       int n_kv_heads, int head_dim, int cache_cap, int ring, int window,
+                       float scale) {
     int st = check_heads(n_q_heads, n_kv_heads, head_dim);
     if (st != ATTN_OK) return st;
     if (n_seq < 0 || (ring != 0 && ring != 1) || !isfinite(scale)) return ATTN_E_RANGE;
@@ -82,17 +85,30 @@ int attn_decode(void* out, const void* q, const void* k_cache,
     if ((long long)cache_cap * head_dim * 2 >= (1LL << 32)) return ATTN_E_RANGE;
     if (n_seq == 0) return ATTN_OK;
     if (!out || !q || !k_cache || !v_cache || !pos) return ATTN_E_NULL;
-    if (!workspace) return ATTN_E_WORKSPACE;
-    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) ||
-        !aligned16(v_cache) || !aligned16(workspace) ||
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
         (reinterpret_cast<uintptr_t>(pos) & 3u) != 0)
         return ATTN_E_ALIGN;
-    const size_t need = attn_decode_workspace_bytes(n_seq, n_q_heads, head_dim, cache_cap);
-    if (need == 0) return ATTN_E_RANGE;
-    if (workspace_bytes < need) return ATTN_E_WORKSPACE;
     if (n_seq > 65535 || n_kv_heads > 65535 ||
         (cache_cap + ATTN_DECODE_CHUNK - 1) / ATTN_DECODE_CHUNK > 0x7FFFFFFF / 2)
         return ATTN_E_RANGE;
+    return ATTN_OK;
+}
+
+extern "C" {
+
+int attn_decode(void* out, const void* q, const void* k_cache,
+                const void* v_cache, const int32_t* pos, int n_seq,
+                int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
+                int ring, int window, float scale, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    const int st = decode_args_status(out, q, k_cache, v_cache, pos, n_seq, n_q_heads,
+                                      n_kv_heads, head_dim, cache_cap, ring, window, scale);
+    if (st != ATTN_OK || n_seq == 0) return st;
+    if (!workspace) return ATTN_E_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_E_ALIGN;
+    const size_t need = attn_decode_workspace_bytes(n_seq, n_q_heads, head_dim, cache_cap);
+    if (need == 0) return ATTN_E_RANGE;
+    if (workspace_bytes < need) return ATTN_E_WORKSPACE;
     hipError_t e = launch_decode(
         static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
         static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
@@ -271,6 +287,9 @@ static int check_prefill(int pos0, int n_rows, int n_q_heads, int n_kv_heads, in
         return ATTN_E_RANGE;
     // one head's cache slice is addressed with 32-bit byte offsets
     if ((long long)cache_cap * head_dim * 2 >= (1LL << 32)) return ATTN_E_RANGE;
+    // the kernels form positions up to the last row's plus one key block in
+    // 32-bit ints (a ring's positions are not bounded by its capacity)
+    if ((long long)pos0 + n_rows + 64 > 0x7FFFFFFFLL) return ATTN_E_RANGE;
     return ATTN_OK;
 }
 

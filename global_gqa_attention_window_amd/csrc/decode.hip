@@ -188,7 +188,30 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     const size_t head_base = ((size_t)s * Hkv + g) * (size_t)cap * D;
     const uint16_t* Kh = kc + head_base;
     const uint16_t* Vh = vc + head_base;
-    const int sub = ring ? t1 % cap : min(t1, cap - 1);     // t1 >= 0 here
+    // Source of a slot no row of the workgroup attends: a slot the last row
+    // attends (its contents are finite, or NaN that belongs in the output).
+    // With PREP the row's own slot is written by this launch, so the source
+    // is another attended slot of the run (its lowest, else its highest);
+    // when the row's own slot is the run's only attended slot, every staged
+    // row of that slot's block is overwritten with the new key and value
+    // once the block has landed (fill_all).
+    int sub = ring ? t1 % cap : min(t1, cap - 1);           // t1 >= 0 here
+    [[maybe_unused]] bool fill_all = false;
+    if constexpr (PREP) {
+        // lowest or highest attended slot of block bb (which holds one; an
+        // empty ballot would keep the last row's slot)
+        auto ends = [&](int bb, bool lowest) {
+            const bool a = lane < WKB && attended(slot0 + bb * WKB + lane, t1, t1m, w_all);
+            const uint64_t bal = __ballot(a);
+            if (bal == 0) return sub;
+            return slot0 + bb * WKB + (lowest ? __builtin_ctzll(bal) : 63 - __builtin_clzll(bal));
+        };
+        const int s_lo = ends(bb_lo, true);
+        const int s_hi = ends(bb_hi, false);
+        if (s_lo != sub) sub = s_lo;
+        else if (s_hi != sub) sub = s_hi;
+        else fill_all = true;
+    }
 
     // DMA instruction i = wave + 4 k of a K or V block moves 1 KiB: block row
     // i at D = 512, rows 16 (i >> 3) + (i & 7) and + 8 at D = 256 (lanes
@@ -457,10 +480,14 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         if constexpr (PREP) {
             if (b == b_slot) {
                 // the row's own key and value over the staged slot contents
+                // (over every row of the block with fill_all: its other rows
+                // were fetched from the slot being written)
                 const int st = (b - bb_lo) & 1;
-                if (tid < 2 * (D / 8)) {
-                    const int part = tid / (D / 8), piece = tid % (D / 8);
-                    uint16_t* dst = (part ? vs[st] : ks[st]) + row_pos<D, WPAD>(r_slot) + 8 * piece;
+                const int n_fill = (fill_all ? WKB : 1) * 2 * (D / 8);
+                for (int idx = tid; idx < n_fill; idx += 256) {
+                    const int r = fill_all ? idx / (2 * (D / 8)) : r_slot;
+                    const int part = (idx / (D / 8)) & 1, piece = idx % (D / 8);
+                    uint16_t* dst = (part ? vs[st] : ks[st]) + row_pos<D, WPAD>(r) + 8 * piece;
                     *reinterpret_cast<u32x4*>(dst) =
                         *reinterpret_cast<const u32x4*>(&kv_new[part][8 * piece]);
                 }

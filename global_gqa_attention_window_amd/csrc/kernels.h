@@ -11,6 +11,13 @@
 
 size_t decode_workspace_bytes(int S, int Hq, int D, int cap);
 
+// attn_decode's argument checks other than its workspace (api.hip); ATTN_OK
+// with S == 0 means there is nothing to launch
+int decode_args_status(const void* out, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* pos, int n_seq, int n_q_heads,
+                       int n_kv_heads, int head_dim, int cache_cap, int ring, int window,
+                       float scale);
+
 hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                          const uint16_t* vc, const int32_t* pos, int S, int Hq,
                          int Hkv, int D, int cap, int ring, int window,

@@ -279,7 +279,8 @@ int attn_decode_prep_fused(void* out, const void* qkv, const void* q_norm_w,
  *   q         device bf16 [n_rows][Hq][D]
  *   k_cache   device bf16 [Hkv][cap][D]
  *   v_cache   device bf16 [Hkv][cap][D]
- *   pos0      position of the first row, >= 0
+ *   pos0      position of the first row, >= 0, with pos0 + n_rows + 64 <=
+ *             INT32_MAX (positions are 32-bit ints), else ATTN_E_RANGE
  *   n_rows    >= 0 (0 launches nothing)
  *   ring      0 linear (pos0 + n_rows <= cap), 1 ring (0 < W <= cap and
  *             cap >= W + n_rows - 1, so no row's keys are overwritten)

@@ -77,8 +77,22 @@ def test_workspace_bytes(ga):
     assert ga.attn_decode_workspace_bytes(-1, 8, 256, 10) == 0
 
 
-# fake device pointers: refusals happen before any use, so these are never read
+# fake device pointers: refusals happen before any use, so these are never read.
+# The refusal tests pass them to real entry points, so they run only where no
+# GPU is visible: if a check ever let a call through, its launch would fail on
+# the host instead of touching unmapped device memory.
 P = 1 << 20
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:          # no torch: no GPU either
+        return False
+
+
+no_gpu = pytest.mark.skipif(_gpu_visible(), reason="fake device pointers; CPU-only checks")
 
 
 def _decode(ga, **kw):
@@ -122,10 +136,12 @@ def _cw(ga, **kw):
     (dict(ws_bytes=100), "ATTN_E_WORKSPACE"),
     (dict(S=1 << 20, cap=1 << 30, Hkv=1 << 10, Hq=1 << 10), "ATTN_E_RANGE"),
 ])
+@no_gpu
 def test_decode_refusals(ga, kw, status):
     assert _decode(ga, **kw) == _status(status)
 
 
+@no_gpu
 def test_decode_zero_streams_is_a_no_op(ga):
     assert _decode(ga, S=0, out=None, q=None, ws=None) == 0
 
@@ -143,16 +159,29 @@ def test_decode_zero_streams_is_a_no_op(ga):
     (dict(pos0=-5), "ATTN_E_RANGE"), (dict(scale=float("-inf")), "ATTN_E_RANGE"),
     (dict(q=P + 6), "ATTN_E_ALIGN"),
 ])
+@no_gpu
 def test_prefill_refusals(ga, kw, status):
     assert _prefill(ga, **kw) == _status(status)
 
 
+@no_gpu
 def test_prefill_refuses_slices_past_32_bit_offsets(ga):
     # one head's cache slice is addressed with 32-bit byte offsets
     assert _prefill(ga, ring=0, window=0, D=512, cap=1 << 22, n=0) == _status("ATTN_E_RANGE")
     assert _prefill(ga, ring=0, window=0, D=512, cap=(1 << 22) - 1, n=0) == 0
 
 
+@no_gpu
+def test_prefill_refuses_positions_past_int32(ga):
+    # a ring's positions grow past its capacity; the kernels add up to one
+    # key block (64) to the last row's position in 32-bit ints
+    imax = 0x7FFFFFFF
+    assert _prefill(ga, pos0=imax - 128 - 64 + 1, n=128) == _status("ATTN_E_RANGE")
+    assert _prefill(ga, pos0=imax, n=1) == _status("ATTN_E_RANGE")
+    assert _prefill(ga, pos0=imax - 64, n=0) == 0
+
+
+@no_gpu
 def test_prefill_edges_accepted_by_checks(ga):
     # exact fits pass the checks; n = 0 returns before any launch
     assert _prefill(ga, n=0, out=None) == 0
@@ -166,6 +195,7 @@ def test_prefill_edges_accepted_by_checks(ga):
     (dict(n=1153), "ATTN_E_CACHE"), (dict(pos0=-1), "ATTN_E_RANGE"),
     (dict(k=P + 2), "ATTN_E_ALIGN"),
 ])
+@no_gpu
 def test_cache_write_refusals(ga, kw, status):
     assert _cw(ga, **kw) == _status(status)
 
@@ -190,10 +220,12 @@ def _rows(ga, **kw):
     (dict(pos=P + 2), "ATTN_E_ALIGN"), (dict(q=P + 8), "ATTN_E_ALIGN"),
     (dict(scale=float("nan")), "ATTN_E_RANGE"), (dict(cap=0), "ATTN_E_CACHE"),
 ])
+@no_gpu
 def test_decode_rows_refusals(ga, kw, status):
     assert _rows(ga, **kw) == _status(status)
 
 
+@no_gpu
 def test_decode_rows_edges_and_workspace(ga):
     assert _rows(ga, S=0, out=None, q=None, ws=None) == 0
     # a ring of exactly W + R - 1 slots passes the geometry check (then n_seq = 0)
@@ -206,6 +238,7 @@ def test_decode_rows_edges_and_workspace(ga):
     assert ga.ATTN_DECODE_MAX_ROWS == 16
 
 
+@no_gpu
 def test_fused_decode_refusals(ga):
     lib = ga._lib
     n = 1 << 34

@@ -119,6 +119,51 @@ def test_prep_fused_equals_prep_then_decode(ga, D, Hq, Hkv, cap, ring, window, v
     assert int(ws[:ga.ATTN_DECODE_COUNTER_BYTES].count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("D,Hq,Hkv,cap,ring,window,pos", [
+    (256, 8, 1, 512, 0, 0, [300]),                  # linear, unwritten slots after t
+    (256, 8, 1, 512, 0, 0, [256]),                  # t alone in its run
+    (256, 8, 1, 512, 0, 1, [200]),                  # window of one: t alone
+    (256, 32, 4, 1024, 1, 1024, [500, 7, 1023]),    # ring not yet filled
+    (512, 32, 2, 32768, 0, 0, [12345, 4096]),       # 16 runs, last-workgroup merge
+    (512, 16, 1, 1024, 1, 512, [700]),              # ring, window inside the filled part
+])
+def test_prep_fused_never_reads_the_slot_it_writes(ga, D, Hq, Hkv, cap, ring, window, pos):
+    """The row's own slot and every slot no position has reached hold NaN
+    before the call (e.g. fresh torch.empty memory).  The fused call writes
+    the row's slot and must give the finite outputs of prologue + decode,
+    whose decode reads the slot after the prologue wrote it."""
+    import torch
+    say("prep fused, poisoned own slot", D, Hq, Hkv, cap, ring, window, pos)
+    S = len(pos)
+    qkv, qw, kw, k, v = _inputs(11 * D + cap + pos[0], S, Hq, Hkv, D, cap)
+    for s, t in enumerate(pos):
+        written = np.arange(cap) < t if not ring else np.arange(cap) < min(t, cap)
+        if ring and t >= cap:
+            written[:] = True
+        k[s, :, ~written] = 0x7FC0
+        v[s, :, ~written] = 0x7FC0
+        k[s, :, _slot(t, cap, ring)] = 0x7FC0
+        v[s, :, _slot(t, cap, ring)] = 0x7FC0
+    f = _freqs(D, 1e4 if D == 256 else 1e6)
+    n = ga.ATTN_DECODE_COUNTER_BYTES + ga.attn_decode_rows_workspace_bytes(S, 1, Hq, D, cap)
+    ws = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    ga.attn_decode_workspace_init(ws)
+    pd = up(np.asarray(pos, np.int32))
+    k1, v1 = up(k), up(v)
+    q_out = _prep(ga, qkv, qw, kw, f, 1e-6, 1, pos, Hq, Hkv, D, k1, v1, ring)
+    o1 = torch.empty((S, 1, Hq, D), dtype=torch.int16, device=DEV)
+    ga.attn_decode_rows_fused(o1, q_out.view(S, 1, Hq, D), k1, v1, pd, S, 1, Hq, Hkv, D, cap,
+                              ring, window, 0.05, ws)
+    k2, v2 = up(k), up(v)
+    o2 = torch.empty((S, Hq, D), dtype=torch.int16, device=DEV)
+    ga.attn_decode_prep_fused(o2, up(qkv), up(qw), up(kw), torch.from_numpy(f).to(DEV), 1e-6,
+                              1, k2, v2, pd, S, Hq, Hkv, D, cap, ring, window, 0.05, ws)
+    a, b = down(o1)[:, 0], down(o2)
+    assert not np.any((a & 0x7FFF) > 0x7F80), "prologue + decode gave NaN"
+    assert np.array_equal(a, b)
+    assert np.array_equal(down(k1), down(k2)) and np.array_equal(down(v1), down(v2))
+
+
 def test_prep_fused_graph_replay(ga):
     """A captured prologue + decode, replayed for new rows and positions: each
     replay writes the row's key/value and equals the eager call."""
