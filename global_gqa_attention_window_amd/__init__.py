@@ -31,6 +31,7 @@ ATTN_P_FP32, ATTN_P_BF16, ATTN_P_BF16X2 = 0, 1, 2
 ATTN_DECODE_CHUNK = 256
 ATTN_DECODE_MAX_ROWS = 16
 ATTN_DECODE_COUNTER_BYTES = 65536
+ATTN_DECODE_SCRATCH_BYTES = 16 << 20
 
 _c_int, _c_void_p, _c_float, _c_size_t = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
 
@@ -38,6 +39,8 @@ _lib.attn_decode_workspace_bytes.restype = _c_size_t
 _lib.attn_decode_workspace_bytes.argtypes = [_c_int] * 4
 _lib.attn_decode.restype = _c_int
 _lib.attn_decode.argtypes = ([_c_void_p] * 5 + [_c_int] * 7 + [_c_float, _c_void_p, _c_size_t, _c_void_p])
+_lib.attn_decode_noalloc.restype = _c_int
+_lib.attn_decode_noalloc.argtypes = [_c_void_p] * 5 + [_c_int] * 7 + [_c_float, _c_void_p]
 _lib.attn_decode_rows_workspace_bytes.restype = _c_size_t
 _lib.attn_decode_rows_workspace_bytes.argtypes = [_c_int] * 5
 _lib.attn_decode_rows.restype = _c_int
@@ -154,6 +157,19 @@ def attn_decode(out, q, k_cache, v_cache, pos, n_seq, n_q_heads, n_kv_heads,
                           n_seq, n_q_heads, n_kv_heads, head_dim, cache_cap, ring,
                           window, float(scale), wp, wb, _stream(stream))
     _ok(st, "attn_decode")
+
+
+def attn_decode_noalloc(out, q, k_cache, v_cache, pos, n_seq, n_q_heads, n_kv_heads,
+                        head_dim, cache_cap, ring, window, scale, stream=None) -> None:
+    """attn_decode with its partials in the library's own device array (no
+    workspace, nothing allocated); calls that overlap on one GPU race."""
+    nq, nc = n_seq * n_q_heads * head_dim, n_seq * n_kv_heads * cache_cap * head_dim
+    st = _lib.attn_decode_noalloc(_arg(out, "out", nq), _arg(q, "q", nq),
+                                  _arg(k_cache, "k_cache", nc), _arg(v_cache, "v_cache", nc),
+                                  _arg(pos, "pos", n_seq, 4), n_seq, n_q_heads, n_kv_heads,
+                                  head_dim, cache_cap, ring, window, float(scale),
+                                  _stream(stream))
+    _ok(st, "attn_decode_noalloc")
 
 
 def attn_decode_rows(out, q, k_cache, v_cache, pos, n_seq, rows, n_q_heads, n_kv_heads,

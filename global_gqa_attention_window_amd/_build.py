@@ -7,7 +7,8 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgqa_attn.so")
-SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill512.hip", "cache_write.hip"]
+SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill512.hip", "cache_write.hip",
+           "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -769,6 +769,13 @@ size_t decode_workspace_bytes(int S, int Hq, int D, int cap) {
     return (size_t)S * Hq * nch * ((size_t)D + 2) * sizeof(float);
 }
 
+size_t decode_partials_bytes(int S, int Hq, int D, int cap) {
+    const size_t nch = ((size_t)cap + CHUNK - 1) / CHUNK;
+    const size_t cpr = (size_t)decode_run_chunks(cap);
+    const size_t nrun = (nch + cpr - 1) / cpr;
+    return (size_t)S * Hq * nrun * ((size_t)D + 2) * sizeof(float);
+}
+
 hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                          const uint16_t* vc, const int32_t* pos, int S, int Hq,
                          int Hkv, int D, int cap, int ring, int window,

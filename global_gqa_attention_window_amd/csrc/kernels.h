@@ -10,6 +10,9 @@
 #include "prologue.h"
 
 size_t decode_workspace_bytes(int S, int Hq, int D, int cap);
+// bytes of partials a one-row decode launch (launch_decode) writes and reads:
+// one fp32 (max, sum, accumulator[D]) per (stream, query head, run of chunks)
+size_t decode_partials_bytes(int S, int Hq, int D, int cap);
 
 // attn_decode's argument checks other than its workspace (api.hip); ATTN_OK
 // with S == 0 means there is nothing to launch

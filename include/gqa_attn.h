@@ -126,6 +126,35 @@ int attn_decode(void* out, const void* q, const void* k_cache,
                 int ring, int window, float scale, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* Bytes of the library's own device array that attn_decode_noalloc keeps
+   its partials in (one array per device, held until the process ends). */
+#define ATTN_DECODE_SCRATCH_BYTES (16u << 20)
+
+/*
+ * attn_decode for callers that cannot allocate device memory: code that a
+ * HIP graph captures, serving loops and harnesses that forbid hipMalloc.
+ * The chunk-run partials go to a fixed array of ATTN_DECODE_SCRATCH_BYTES
+ * inside the library instead of a caller's workspace; the call allocates
+ * nothing and issues no memset.  Kernels, arithmetic and output bits are
+ * attn_decode's.
+ *
+ * Arguments and errors as attn_decode, without the workspace, plus:
+ *   ATTN_E_WORKSPACE  the partials do not fit the array: S * Hq * runs *
+ *                     (D + 2) * 4 bytes > ATTN_DECODE_SCRATCH_BYTES, runs =
+ *                     ceil(n / c), n = ceil(cap / 256) chunks, c = floor(n / 16)
+ *                     clamped to 1..8 (e.g. 8 streams x 32 heads at D = 512
+ *                     over 32768 keys, or one stream over 262144, use 8.4 MB)
+ *   ATTN_E_LAUNCH     also when the array's device address cannot be found
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents (nothing in it needs to start at zero): calls that may
+ * overlap on one device (other streams, other host threads) race and must
+ * be ordered by the caller.
+ */
+int attn_decode_noalloc(void* out, const void* q, const void* k_cache,
+                        const void* v_cache, const int32_t* pos, int n_seq,
+                        int n_q_heads, int n_kv_heads, int head_dim, int cache_cap,
+                        int ring, int window, float scale, void* stream);
+
 /* Largest decode window (rows per stream) of attn_decode_rows. */
 #define ATTN_DECODE_MAX_ROWS 16
 

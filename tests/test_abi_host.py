@@ -254,3 +254,28 @@ def test_fused_decode_refusals(ga):
     assert lib.attn_decode_workspace_init(None, 1 << 20, None) == _status("ATTN_E_WORKSPACE")
     assert lib.attn_decode_workspace_init(P, 1000, None) == _status("ATTN_E_WORKSPACE")
     assert lib.attn_decode_workspace_init(P + 4, 1 << 20, None) == _status("ATTN_E_ALIGN")
+
+
+@no_gpu
+def test_noalloc_decode_refusals(ga):
+    lib = ga._lib
+
+    def call(**kw):
+        a = dict(out=P, q=P, k=P, v=P, pos=P, S=8, Hq=32, Hkv=2, D=512, cap=32768, ring=0,
+                 window=0, scale=0.044)
+        a.update(kw)
+        return lib.attn_decode_noalloc(a["out"], a["q"], a["k"], a["v"], a["pos"], a["S"],
+                                       a["Hq"], a["Hkv"], a["D"], a["cap"], a["ring"],
+                                       a["window"], a["scale"], None)
+    # partials past the library's array: 8 x 32 heads x 32 runs x 514 x 4 B > 16 MiB
+    assert 8 * 32 * 32 * 514 * 4 > ga.ATTN_DECODE_SCRATCH_BYTES
+    assert call(cap=65536) == _status("ATTN_E_WORKSPACE")
+    assert call(S=17) == _status("ATTN_E_WORKSPACE")
+    # the other checks are attn_decode's
+    assert call(S=0, out=None) == 0
+    assert call(out=None) == _status("ATTN_E_NULL")
+    assert call(D=128) == _status("ATTN_E_HEAD_DIM")
+    assert call(Hq=31) == _status("ATTN_E_GQA")
+    assert call(q=P + 2) == _status("ATTN_E_ALIGN")
+    assert call(ring=1, window=40000) == _status("ATTN_E_WINDOW")
+    assert call(scale=float("nan")) == _status("ATTN_E_RANGE")
