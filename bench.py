@@ -19,8 +19,13 @@ workloads of 512 keys, of 8 streams over a 1024-slot sliding ring and of 8
 streams over 32768 global-layer keys against HBM bandwidth (the two small
 ones also cold, rotating over K/V sets larger than the last-level cache);
 decode windows (16 rows a stream, 8 streams, 32768 keys) against the bf16
-matrix-core peak; and the attainable copy bandwidth and bf16 matrix-product
-rate of library kernels on the part, beside the published peaks.
+matrix-core peak; the attainable rates on the part beside the published
+peaks (library kernels: a device copy and a bf16 matrix product; kernels of
+our own: a read-only HBM stream and a loop of bf16 matrix products); the
+shader clock measured right after the timed steps (cycle counter against the
+100 MHz real-time counter); and the oracle on the other workloads (decodes in
+GB/s of attended K/V, the 8k prompt in tokens/s) with the host's CPU count
+and model.
 """
 from __future__ import annotations
 
@@ -280,6 +285,93 @@ def decode_cold(ga, torch, dev, min_bytes: int = 600 << 20):
     return res
 
 
+def calib_lib():
+    """The calibration kernels (libgqa_calib.so, built with the package), or
+    None when they were not built."""
+    import ctypes
+    path = os.path.join(ROOT, "global_gqa_attention_window_amd", "libgqa_calib.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.calib_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.calib_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.calib_clock.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    return lib
+
+
+def gpu_clock_mhz(torch, dev):
+    """The shader clock right now: each of 256 workgroups (one per CU) times
+    a matrix-core loop of about a millisecond with the cycle counter and the
+    100 MHz real-time counter; the median ratio in MHz.  Run right after a
+    timed region, it tells the clock that region ran at (None without the
+    calibration library)."""
+    lib = calib_lib()
+    if lib is None:
+        return None
+    out = torch.zeros(3 * 256, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    assert lib.calib_clock(20000, out.data_ptr(), 256, stream) == 0
+    torch.cuda.synchronize()
+    o = out.view(256, 3).cpu().tolist()
+    r = sorted(c / t * 100.0 for c, t, _ in o if t > 0)
+    return round(r[len(r) // 2], 1) if r else None
+
+
+def attainable_kernels(torch, dev):
+    """Measured ceilings of this part from kernels of our own: a read-only
+    stream over 1 GiB (every byte read once with 16-byte loads over the whole
+    chip; the best of a few grid sizes and loads in flight) and a loop of bf16
+    16x16x32 matrix products from registers, two waves on every SIMD (16384
+    flops each); the shader clock measured right after each."""
+    lib = calib_lib()
+    if lib is None:
+        return {"error": "libgqa_calib.so not built"}
+    stream = torch.cuda.current_stream().cuda_stream
+    res = {}
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    sink = torch.empty(8192 * 256, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    for grid, unroll in ((2048, 8), (2048, 16), (4096, 4), (4096, 8), (8192, 4)):
+        for _ in range(2):
+            assert lib.calib_read_stream(src.data_ptr(), n, sink.data_ptr(), grid, unroll,
+                                         stream) == 0
+        torch.cuda.synchronize()
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            lib.calib_read_stream(src.data_ptr(), n, sink.data_ptr(), grid, unroll, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        if best is None or gbs > best[0]:
+            best = (gbs, grid, unroll)
+    gbs, grid, unroll = best
+    res["read_stream"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                          "bytes": n, "grid": grid, "loads_in_flight": unroll,
+                          "clock_MHz_after": gpu_clock_mhz(torch, dev)}
+    del src, sink
+    grid, iters = 512, 40000
+    sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    assert lib.calib_mfma_loop(100, sink.data_ptr(), grid, stream) == 0
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        lib.calib_mfma_loop(iters, sink.data_ptr(), grid, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    flops = 3 * grid * 4 * iters * 8 * 16384
+    tf = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    res["mfma_loop_bf16"] = {"TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                             "clock_MHz_after": gpu_clock_mhz(torch, dev)}
+    del sink
+    torch.cuda.empty_cache()
+    return res
+
+
 def attainable(torch, dev):
     """Attainable rates on this part with library kernels, beside the
     published peaks: a 1 GiB device-to-device copy (bytes read + written per
@@ -318,12 +410,33 @@ def attainable(torch, dev):
             "bf16_gemm_frac_peak": round(mm_tf / PEAK_BF16_TFLOPS, 4)}
 
 
+def host_cpu():
+    """The host's logical CPUs (this process's affinity and os.cpu_count())
+    and its CPU model (/proc/cpuinfo)."""
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"logical_cpus_affinity": len(os.sched_getaffinity(0)),
+            "os_cpu_count": os.cpu_count(), "cpu_model": model}
+
+
+def blas_threads():
+    from threadpoolctl import threadpool_info
+    return int(max([p.get("num_threads", 1) for p in threadpool_info()] + [1]))
+
+
 def cpu_baseline(q, k, v, w, n_rows_sample: int):
     """The oracle as it stands, on prompt rows spread evenly over the prompt
     (per-row cost grows with position, so an even spread has the prompt's
-    mean cost), every head; tokens/s = rows / seconds."""
+    mean cost), every head; tokens/s = rows / seconds.  `cores` is the BLAS
+    thread count the oracle's float64 products ran on (it has no other
+    parallelism); the host's CPU count and model are beside it."""
     import numpy as np
-    from threadpoolctl import threadpool_info
 
     from oracle import attn_ref
     from oracle.contract import key_block
@@ -334,12 +447,68 @@ def cpu_baseline(q, k, v, w, n_rows_sample: int):
     attn_ref.prefill(q, k, v, 0, w.Hkv, w.window, w.scale, w.p_mode,
                      key_block(w.D, w.p_mode), rows=rows, row_batch=8)
     dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": round(n_rows_sample / dt, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": round(n_rows_sample / dt, 3), "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle", "host": host_cpu(),
             "sample": f"{n_rows_sample} prompt rows evenly spread over positions 0..{n - 1} "
                       f"of the 32768-token prompt, all 32 heads, float64 NumPy; "
                       f"{dt:.1f} s"}
+
+
+def cpu_oracle_workloads(n_prompt_rows: int = 256):
+    """The oracle as it stands on the other workloads, in the GPU's units:
+    the one-row decodes in GB/s of attended K/V (+ q, out) — the two small
+    ones whole, the 8-stream 32768-key decode on one stream of the eight, the
+    262144-key decode on one KV head of the two (its 16 query heads) — and the
+    8192-token sliding prompt on rows spread evenly over it, in tokens/s."""
+    import numpy as np
+
+    from oracle import attn_ref
+    from oracle.contract import key_block
+    from synthetic.gen import WORKLOADS, decode_inputs, prefill_inputs, randn_bf16_bits
+
+    res = {"cores": blas_threads()}
+
+    def dec(name, q, k, v, pos, Hkv, ring, window, scale, note):
+        S, Hq, D = q.shape
+        cap = k.shape[2]
+        keys = sum(min(cap, int(p) + 1) if window <= 0 else min(cap, int(p) + 1, window)
+                   for p in pos)
+        nbytes = 2 * Hkv * keys * D * 2 + 2 * S * Hq * D * 2
+        t0 = time.perf_counter()
+        attn_ref.decode(q, k, v, pos, Hkv, ring, window, scale)
+        dt = time.perf_counter() - t0
+        res[name] = {"GB/s": round(nbytes / dt / 1e9, 4), "s": round(dt, 3), "bytes": nbytes,
+                     "sample": note}
+
+    for name in ("decode_g8_d256_512", "decode_sliding_ring1024"):
+        w = WORKLOADS[name]
+        q, k, v, pos = decode_inputs(w)
+        dec(name, q, k, v, pos, w.Hkv, w.ring, w.window, w.scale, "whole workload")
+    w = WORKLOADS["decode_global_32k"]
+    q, k, v, pos = decode_inputs(w, S=1, pos=w.pos[:1])
+    dec(w.name, q, k, v, pos, w.Hkv, w.ring, w.window, w.scale, "one stream of the eight")
+    del q, k, v
+    wp = WORKLOADS["prefill_global_32k"]
+    cap = wp.extra["decode_cap"]
+    rng = np.random.default_rng(wp.extra["decode_seed"])
+    q = randn_bf16_bits(rng, (1, wp.Hq // wp.Hkv, wp.D))
+    k = randn_bf16_bits(rng, (1, 1, cap, wp.D))
+    v = randn_bf16_bits(rng, (1, 1, cap, wp.D))
+    dec("decode_262144", q, k, v, [wp.extra["decode_pos"]], 1, 0, 0, wp.scale,
+        "one KV head of the two (its 16 query heads)")
+    del q, k, v
+    w = WORKLOADS["prefill_sliding_8k"]
+    q, k, v = prefill_inputs(w)
+    n = w.n_rows
+    rows = np.linspace(n // (2 * n_prompt_rows), n - 1, n_prompt_rows).astype(np.int64)
+    t0 = time.perf_counter()
+    attn_ref.prefill(q, k, v, 0, w.Hkv, w.window, w.scale, w.p_mode, key_block(w.D, w.p_mode),
+                     rows=rows, row_batch=16)
+    dt = time.perf_counter() - t0
+    res[w.name] = {"tokens_per_s": round(n_prompt_rows / dt, 3), "s": round(dt, 3),
+                   "sample": f"{n_prompt_rows} prompt rows evenly spread over the 8192, "
+                             "all 32 heads"}
+    return res
 
 
 def main():
@@ -416,6 +585,7 @@ def main():
         dec_ms += ev_dec[0].elapsed_time(ev_dec[1])
     wall = time.perf_counter() - t0
     torch.cuda.synchronize()
+    step_clock = gpu_clock_mhz(torch, dev)
 
     ms_step = wall * 1e3 / args.steps
     tokens = n + 1
@@ -457,6 +627,7 @@ def main():
                     "kernel_ms_per_prompt": round(pf_ms / args.steps, 3)},
         "decode": {"us": round(dec_us, 2), "GB/s": round(dec_gbs, 1),
                    "frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4), "bytes": dec_bytes},
+        "gpu_clock_MHz_after_steps": step_clock,
     }
     # the same decode call 20 times back to back (its 1 GiB K/V still comes
     # from HBM each time: it is four times the last-level cache)
@@ -480,8 +651,10 @@ def main():
     rec["decode_configs_cold"] = decode_cold(ga, torch, dev)
     rec["decode_windows"] = decode_windows(ga, torch, dev)
     rec["attainable"] = attainable(torch, dev)
+    rec["attainable"].update(attainable_kernels(torch, dev))
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(q_np, k_np, v_np, w, args.cpu_rows)
+        rec["cpu_oracle_workloads"] = cpu_oracle_workloads()
     print(json.dumps(rec), flush=True)
 
 

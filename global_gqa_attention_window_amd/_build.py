@@ -1,4 +1,5 @@
-"""Build the gfx950 shared library libgqa_attn.so in-tree with hipcc."""
+"""Build the gfx950 shared library libgqa_attn.so in-tree with hipcc (and the
+benchmark's calibration kernels, libgqa_calib.so)."""
 from __future__ import annotations
 
 import os
@@ -7,6 +8,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgqa_attn.so")
+CALIB = os.path.join(PKG, "libgqa_calib.so")
 SOURCES = ["api.hip", "decode.hip", "prefill.hip", "prefill512.hip", "cache_write.hip",
            "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -48,9 +50,14 @@ def build(verbose: bool = False) -> str:
         objs.append(obj)
     tmp = LIB + ".tmp"
     msgs += _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    # the benchmark's calibration kernels, a library of their own
+    cobj = os.path.join(objdir, "calib.o")
+    msgs += _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, "calib.hip"), "-o", cobj])
+    msgs += _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", cobj, "-o", CALIB + ".tmp"])
+    os.replace(CALIB + ".tmp", CALIB)
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
     return LIB
 
 

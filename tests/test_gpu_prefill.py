@@ -1,9 +1,11 @@
 """GPU parity of attn_cache_write + attn_prefill against the CPU oracle.
 
 Prompt rows are fed chunk by chunk (cache write, then attention) exactly as
-the benchmark feeds them.  The full-size workloads are checked on sampled rows
-(every head, every d) computed by the oracle one row batch at a time; the
-small cases are checked on every output.
+the benchmark feeds them.  The full-size workloads run through the GPU once
+each: the 8k sliding prompt is checked on every output, the 32k global prompt
+on its whole last chunk (the longest key walk), a whole middle chunk and
+sampled rows (every head, every d of each), the oracle computing one row
+batch at a time; the small cases are checked on every output.
 """
 import numpy as np
 import pytest
@@ -32,40 +34,71 @@ def _check(tag, got, ref):
     assert res["bit_equal"] >= 0.9, (tag, res)
 
 
-def _sample_rows(n, chunk, rng, n_random=96):
-    rows = set(range(0, min(n, chunk)))                 # the first chunk whole
-    mid = (n // chunk // 2) * chunk
-    rows |= set(range(mid, min(n, mid + chunk)))        # a middle chunk whole
-    rows |= set(range(max(0, n - 16), n))               # the last rows
-    rows |= set(int(x) for x in rng.integers(0, n, n_random))
-    return np.array(sorted(rows))
-
-
-def test_prefill_sliding_8k_full(ga):
+@pytest.fixture(scope="module")
+def sliding_8k(ga):
+    """The 8192-token sliding prompt through the GPU once (128-row chunks)."""
     w = WORKLOADS["prefill_sliding_8k"]
     say("prefill workload", w.name)
     q, k, v = prefill_inputs(w)
     got, _ = run_prefill(ga, q, k, v, w.Hkv, w.cap, w.ring, w.window, w.scale,
                          w.p_mode, w.chunk)
-    rows = _sample_rows(w.n_rows, w.chunk, np.random.default_rng(1))
-    ref = attn_ref.prefill(q, k, v, 0, w.Hkv, w.window, w.scale, w.p_mode,
-                           key_block(w.D, w.p_mode), rows=rows)
-    _check(w.name, got[rows], ref)
+    return w, q, k, v, got
 
 
-def test_prefill_global_32k_full(ga):
+@pytest.fixture(scope="module")
+def global_32k(ga):
+    """The 32768-token global prompt through the GPU once (512-row chunks)."""
     w = WORKLOADS["prefill_global_32k"]
     say("prefill workload", w.name)
     q, k, v = prefill_inputs(w)
     got, _ = run_prefill(ga, q, k, v, w.Hkv, w.cap, w.ring, w.window, w.scale,
                          w.p_mode, w.chunk)
+    return w, q, k, v, got
+
+
+def _oracle_rows(w, q, k, v, rows, row_batch):
+    return attn_ref.prefill(q, k, v, 0, w.Hkv, w.window, w.scale, w.p_mode,
+                            key_block(w.D, w.p_mode), rows=rows, row_batch=row_batch)
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_prefill_sliding_8k_every_row(sliding_8k, part):
+    """Every row of the 8k sliding prompt, every head and d, in four parts."""
+    w, q, k, v, got = sliding_8k
+    rows = np.arange(part * 2048, (part + 1) * 2048)
+    say("rows", rows[0], "..", rows[-1])
+    _check(f"{w.name} rows {rows[0]}..{rows[-1]}", got[rows], _oracle_rows(w, q, k, v, rows, 64))
+
+
+def test_prefill_global_32k_sampled(global_32k):
+    w, q, k, v, got = global_32k
     rng = np.random.default_rng(2)
     rows = np.array(sorted(set(range(0, 40)) | set(range(16384, 16400)) |
                            set(range(w.n_rows - 24, w.n_rows)) |
                            set(int(x) for x in rng.integers(0, w.n_rows, 40))))
-    ref = attn_ref.prefill(q, k, v, 0, w.Hkv, w.window, w.scale, w.p_mode,
-                           key_block(w.D, w.p_mode), rows=rows, row_batch=32)
-    _check(w.name, got[rows], ref)
+    _check(w.name, got[rows], _oracle_rows(w, q, k, v, rows, 32))
+
+
+@pytest.mark.parametrize("part", range(8))
+def test_prefill_global_32k_last_chunk(global_32k, part):
+    """The whole last 512-row chunk (the longest key walk: 32256..32767 keys),
+    every head and d, in eight parts of 64 rows."""
+    w, q, k, v, got = global_32k
+    rows = np.arange(w.n_rows - w.chunk + 64 * part, w.n_rows - w.chunk + 64 * (part + 1))
+    say("rows", rows[0], "..", rows[-1])
+    _check(f"{w.name} last chunk rows {rows[0]}..{rows[-1]}", got[rows],
+           _oracle_rows(w, q, k, v, rows, 32))
+
+
+@pytest.mark.parametrize("part", range(4))
+def test_prefill_global_32k_middle_chunk(global_32k, part):
+    """A whole middle 512-row chunk (rows 16384..16895), every head and d,
+    in four parts of 128 rows."""
+    w, q, k, v, got = global_32k
+    rows = np.arange(16384 + 128 * part, 16384 + 128 * (part + 1))
+    say("rows", rows[0], "..", rows[-1])
+    _check(f"{w.name} middle chunk rows {rows[0]}..{rows[-1]}", got[rows],
+           _oracle_rows(w, q, k, v, rows, 32))
 
 
 @pytest.mark.parametrize("D,Hq,Hkv,ring,cap,window,chunk,n,pos0,p_mode", [
