@@ -30,7 +30,7 @@ ATTN_OK = 0
 ATTN_P_FP32, ATTN_P_BF16, ATTN_P_BF16X2 = 0, 1, 2
 ATTN_DECODE_CHUNK = 256
 ATTN_DECODE_MAX_ROWS = 16
-ATTN_DECODE_COUNTER_BYTES = 65536
+ATTN_DECODE_COUNTER_BYTES = 262144
 ATTN_DECODE_SCRATCH_BYTES = 16 << 20
 
 _c_int, _c_void_p, _c_float, _c_size_t = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t

@@ -156,8 +156,9 @@ static int decode_rows_call(void* out, const void* q, const void* k_cache, const
         return ATTN_E_RANGE;
     // one head's cache slice is addressed with 32-bit byte offsets
     if ((long long)cache_cap * head_dim * 2 >= (1LL << 32)) return ATTN_E_RANGE;
-    // four counters per (stream, KV head) in the fused counter area
-    if (fused && (long long)n_seq * n_kv_heads * 4 * 4 > ATTN_DECODE_COUNTER_BYTES)
+    // sixteen counters per (stream, KV head) in the fused counter area (one
+    // per workgroup of the item: up to 16 column tiles at head dim 256)
+    if (fused && (long long)n_seq * n_kv_heads * 16 * 4 > ATTN_DECODE_COUNTER_BYTES)
         return ATTN_E_RANGE;
     if (n_seq == 0) return ATTN_OK;
     if (prep) {

@@ -26,12 +26,20 @@ constexpr int CHUNK = ATTN_DECODE_CHUNK;
 // window; PR #1183 engine note: windows of up to 16 rows a stream).
 //
 // A matrix-core column is one (row, query head) pair: a 16-column tile holds
-// RPT = 16 / G rows of the G query heads of a KV head.  A workgroup of four
-// waves takes 4 / DS column tiles of one (stream, KV head, run of chunks);
-// the DS waves of a tile split its output d range (all of them form the
-// tile's scores, so a column's arithmetic is the same for every DS).  32-key
-// blocks of K and V are staged in LDS by direct global->LDS loads, two
-// stages shared by the four waves.  Per block and column:
+// RPT = 16 / G rows of the G query heads of a KV head.  32-key blocks of K
+// and V are staged in LDS by direct global->LDS loads shared by a
+// workgroup's four waves.  At head dim 512 a workgroup takes 4 / DS column
+// tiles of one (stream, KV head, run of chunks); the DS waves of a tile split
+// its output d range (all of them form the tile's scores, so a column's
+// arithmetic is the same for every DS); two block stages.  At head dim 256 a
+// workgroup takes one tile: the run's even blocks go to waves 0 and 1 and its
+// odd blocks to waves 2 and 3, each pair splitting d in two, so a block's K
+// rows are read and its scores formed by two waves instead of four; each
+// block set keeps its own online softmax and the two join once at the end
+// (M = the larger reference maximum, each set weighted by 2^(m - M)); a pair
+// of blocks lands while the previous pair is multiplied (four stages).  Every
+// R takes the same per-column steps, one tile per workgroup.  Per block and
+// column:
 //   S^T = K . Q^T               bf16 products, two 16-key tiles;
 //   reference maximum           as in the one-row kernel (moves only when the
 //                               block maximum passes it by 8), so p <= 2^8;
@@ -90,7 +98,15 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
                         int R, int Hq, int Hkv, int G, int RPT, int NT, int CG,
                         int n_items, int cap, int nrun, int cpr, int ring, int window,
                         float c, PrepArgs pa) {
-    constexpr int WC = 4 / DS;                  // column tiles per workgroup
+    // Head dim 256: two block sets (KP).  A workgroup takes one column tile;
+    // waves 0, 1 take the even blocks of the run and waves 2, 3 the odd ones,
+    // each pair splitting the d range in two (DS = 2).  A wave reads only its
+    // own blocks' K and V rows and forms their scores once, and the two sets
+    // keep their own online softmax, joined once at the end.  Head dim 512
+    // keeps one set: the DS waves of a tile all form its scores.
+    constexpr bool KP = D == 256;
+    static_assert(!KP || DS == 2, "two block sets take two d halves");
+    constexpr int WC = KP ? 1 : 4 / DS;         // column tiles per workgroup
     constexpr int QST = D / 32;                 // reduction steps of a score
     constexpr int DTW = D / 16 / DS;            // 16-wide d tiles of this wave
     constexpr int LPR = D / 8;                  // lanes moving one row per DMA
@@ -106,12 +122,14 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     // matrix-bound, and the single-launch form serves short runs where the
     // barrier inside each block costs more than the deeper prefetch gains:
     // those move K and V one block ahead, with no barrier inside a block
-    constexpr bool K2 = DS >= 2 && !FUSE;
+    constexpr bool K2 = DS >= 2 && !FUSE && !KP;
+    // stages: two blocks (KP: two pairs of blocks, one in use, one landing)
+    constexpr int NST = KP ? 4 : 2;
     static_assert(NIW * 4 == NI && NG * VG == DTW && QST >= KPF && (2 * NIW) % QST == 0,
                   "shapes");
 
-    __shared__ __attribute__((aligned(16))) uint16_t ks[2][BLK];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[2][BLK];
+    __shared__ __attribute__((aligned(16))) uint16_t ks[NST][BLK];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[NST][BLK];
     // the row's new key and value (PREP)
     __shared__ __attribute__((aligned(16))) uint16_t kv_new[PREP ? 2 : 1][PREP ? D : 8];
 
@@ -132,8 +150,9 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     const int s = u / (nrun * Hkv);
 
     // this wave: column tile ct (RPT rows x G heads), d part dp
-    const int ct = cgi * WC + wave / DS;
-    const int dp = wave % DS;
+    const int ct = cgi * WC + (KP ? 0 : wave / DS);
+    const int dp = KP ? (wave & 1) : wave % DS;
+    const int set = KP ? (wave >> 1) : 0;       // block set (parity of the run's block)
     const int rr = ct * RPT + col / G;
     const int h = g * G + col % G;
     const bool cv = ct < NT && col < RPT * G && rr < R;
@@ -273,11 +292,33 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
                (window <= 0 || pl >= t1 - window + 1);
     };
 
+    // KP: block pair j (blocks 2 j, 2 j + 1 of the run, those the workgroup's
+    // rows attend) into stages 2 ((j - jlo) & 1) + {0, 1}
+    const int jlo = bb_lo >> 1, jhi = bb_hi >> 1;
+    auto issue_pair = [&](int j) {
+        const int sp = 2 * ((j - jlo) & 1);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int b = 2 * j + e;
+            if (b >= bb_lo && b <= bb_hi) {
+                uint32_t vo[NIW];
+                dma_plan(b, vo);
+#pragma unroll
+                for (int k = 0; k < NIW; ++k) {
+                    dma_one(Kh, ks[sp + e], vo, k);
+                    dma_one(Vh, vs[sp + e], vo, k);
+                }
+            }
+        }
+    };
     // the first block's K and V go out before anything else, then the second
     // block's K (K runs two blocks ahead of its use, V one; with PREP the
     // second K stage holds the rotary table until the loop starts, so that
-    // block's K goes out once the table has been read)
-    {
+    // block's K goes out once the table has been read); KP: the first pair
+    // (with PREP the table sits in the second pair's K stage)
+    if constexpr (KP) {
+        issue_pair(jlo);
+    } else {
         uint32_t vo0[NIW];
         dma_plan(bb_lo, vo0);
 #pragma unroll
@@ -306,7 +347,7 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         u32x4 kvx[QST];
         load_row<D>(qreg, pa.qkv + ((size_t)s * (Hq + 2 * Hkv) + h) * D, grp, cv);
         if (owner) load_kv<D>(kvx, pa, s, g, Hq, Hkv, lane, wave);
-        float* cs = reinterpret_cast<float*>(&ks[1][0]);
+        float* cs = reinterpret_cast<float*>(&ks[KP ? 2 : 1][0]);
         rope_table<D>(cs, pa.inv_freq, p0, tid, 256);
         norm_row<D>(qreg, pa.q_w, grp, pa.eps);
         if (owner) norm_kv<D>(kvx, pa, lane, wave);
@@ -470,6 +511,35 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         }
     };
 
+    if constexpr (KP) {
+        for (int j = jlo; j <= jhi; ++j) {
+            // pair j has landed and every wave is done with pair j - 1, whose
+            // stages take pair j + 1 (and, with PREP, the rotary table has
+            // been read)
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            const int sp = 2 * ((j - jlo) & 1);
+            if constexpr (PREP) {
+                if (j == (b_slot >> 1) && b_slot >= 0) {
+                    // the row's own key and value over the staged slot
+                    // contents (over every row of the block with fill_all)
+                    const int st = sp + (b_slot & 1);
+                    const int n_fill = (fill_all ? WKB : 1) * 2 * (D / 8);
+                    for (int idx = tid; idx < n_fill; idx += 256) {
+                        const int r = fill_all ? idx / (2 * (D / 8)) : r_slot;
+                        const int part = (idx / (D / 8)) & 1, piece = idx % (D / 8);
+                        uint16_t* dst = (part ? vs[st] : ks[st]) + row_pos<D, WPAD>(r) + 8 * piece;
+                        *reinterpret_cast<u32x4*>(dst) =
+                            *reinterpret_cast<const u32x4*>(&kv_new[part][8 * piece]);
+                    }
+                    __syncthreads();
+                }
+            }
+            if (j + 1 <= jhi) issue_pair(j + 1);
+            const int b = 2 * j + set;
+            if (b >= bb_lo && b <= bb_hi) block(b, sp + set, std::false_type{}, std::false_type{});
+        }
+    } else {
     for (int b = bb_lo; b <= bb_hi; ++b) {
         // block b has landed (every wave's share; only block b + 1's K, issued
         // last, may still be in flight), and every wave is done with block
@@ -507,6 +577,49 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         else block(b, st, std::false_type{}, std::false_type{});
     }
     }
+    }
+
+    if constexpr (KP) {
+        // the odd set hands its state to the even set through LDS (the
+        // stages are free once every wave is past its last block); per lane
+        // and element: M = max(m_even, m_odd), each set weighted by
+        // 2^(m - M) (0 for a set with no attended key), the two terms added
+        __syncthreads();
+        float* xs = reinterpret_cast<float*>(&ks[0][0]);
+        constexpr int XN = 4 * DTW + 2;
+        float* xl = xs + dp * XN * 64 + lane;
+        if (set == 1) {
+#pragma unroll
+            for (int dt = 0; dt < DTW; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xl[(4 * dt + i) * 64] = acc[dt][i];
+            xl[(4 * DTW) * 64] = m_run;
+            xl[(4 * DTW + 1) * 64] = l_run;
+        }
+        __syncthreads();
+        if (set == 0) {
+#pragma clang fp contract(off)
+            const float m1 = xl[(4 * DTW) * 64];
+            const float l1 = xl[(4 * DTW + 1) * 64];
+            const float M = fmaxf(m_run, m1);
+            const float w0 = m_run == -INFINITY ? 0.f : fast_exp2(m_run - M);
+            const float w1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - M);
+#pragma unroll
+            for (int dt = 0; dt < DTW; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a0 = acc[dt][i] * w0;
+                    const float a1 = xl[(4 * dt + i) * 64] * w1;
+                    acc[dt][i] = a0 + a1;
+                }
+            const float l0w = l_run * w0;
+            const float l1w = l1 * w1;
+            l_run = l0w + l1w;
+            m_run = M;
+        }
+    }
+    // the waves that hold a column's final state (KP: the even set)
+    const bool cvo = cv && set == 0;
 
     const float l_tot = xsum4(l_run);
     // lane holds d = dp D / DS + 16 dt + 4 grp + i of its column in acc[dt][i]
@@ -525,11 +638,11 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     };
     if constexpr (FUSE) {
         if (nrun == 1) {
-            if (cv) store_out(acc, l_tot);
+            if (cvo) store_out(acc, l_tot);
             return;
         }
     }
-    if (cv) {
+    if (cvo) {
         if (dp == 0 && grp == 0) {
             part_ml[2 * pidx + 0] = m_run;
             part_ml[2 * pidx + 1] = l_tot;
@@ -556,7 +669,7 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         }
         __syncthreads();
         if (!s_last) return;
-        if (!cv) return;
+        if (!cvo) return;
         {
             // the merge kernel's arithmetic for nrun <= MW: M the largest run
             // maximum; each run's weighted sums round once (wt l and wt acc,
@@ -814,10 +927,11 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
     const int G = Hq / Hkv;
     const int RPT = 16 / G;                      // rows per 16-column tile
     const int NT = (R + RPT - 1) / RPT;          // column tiles of a window
-    // four waves a workgroup: one tile split four ways over d, two tiles two
-    // ways, or four tiles (three leave one wave idle)
-    const int DS = NT == 1 ? 4 : (NT == 2 ? 2 : 1);
-    const int WC = 4 / DS;
+    // four waves a workgroup: at head dim 512 one tile split four ways over
+    // d, two tiles two ways, or four tiles (three leave one wave idle); at
+    // head dim 256 one tile, two block sets by two d halves
+    const int DS = D == 256 ? 2 : (NT == 1 ? 4 : (NT == 2 ? 2 : 1));
+    const int WC = D == 256 ? 1 : 4 / DS;
     const int CG = (NT + WC - 1) / WC;           // workgroups per item
     const int nch = (cap + CHUNK - 1) / CHUNK;
     const int cpr = decode_run_chunks(cap);
@@ -847,8 +961,13 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
     } while (0)
     if (prep && R != 1) return hipErrorInvalidValue;       // the prologue serves one row
     if (D == 256) {
-        if (one) ROWS_DS(256, true);
-        else ROWS_DS(256, false);
+        if (one) {
+            if (prep) ROWS_LAUNCH(256, 2, true, true);
+            else ROWS_LAUNCH(256, 2, true, false);
+        } else {
+            if (prep) ROWS_LAUNCH(256, 2, false, true);
+            else ROWS_LAUNCH(256, 2, false, false);
+        }
     } else {
         if (one) ROWS_DS(512, true);
         else ROWS_DS(512, false);

@@ -98,7 +98,9 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_q_heads, int head_dim,
  * run c of consecutive 256-slot chunks (1 to 8 chunks, fixed by cap alone)
  * yields m_c (a reference maximum within 8 of the run's largest score, in
  * log2 units), l_c = sum 2^(s log2(e) - m_c) and acc_c = the same weights
- * times v; runs merge in ascending order over M = max m_c; out =
+ * times v (at head dim 256 the run's even and odd 32-slot blocks are summed
+ * apart, each against its own reference maximum, and joined once); runs
+ * merge in ascending order over M = max m_c; out =
  * bf16(sum e^(m_c - M) acc_c / sum e^(m_c - M) l_c).  Scores are scale * q.k
  * with fp32 accumulation; probabilities stay fp32, never rounded to bf16
  * (each enters the P.V products as three bf16 pieces whose sum is exactly
@@ -207,7 +209,7 @@ int attn_decode_rows(void* out, const void* q, const void* k_cache,
                      size_t workspace_bytes, void* stream);
 
 /* Bytes at the start of a fused decode's workspace that hold its counters. */
-#define ATTN_DECODE_COUNTER_BYTES 65536
+#define ATTN_DECODE_COUNTER_BYTES 262144
 
 /*
  * attn_decode_rows in one launch where it can (PR #975 decode commits: with
