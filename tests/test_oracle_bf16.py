@@ -2,8 +2,8 @@
 
 The oracle rounds float64 directly to bf16, ties to even.  Pins: the value
 the pages print (tests/golden/bf16_pages.txt), the textbook integer form of
-float32 -> bf16 rounding over a large sample of float32 patterns and every
-exponent's tie neighbourhood, torch's own conversion, an exact-fraction
+float32 -> bf16 rounding over every float32 pattern (and, cheaply, a sample
+plus every exponent's tie neighbourhood), torch's own conversion, an exact-fraction
 implementation (oracle/brute.py) on float64 inputs, and the special cases
 (double rounding, subnormal ties, the normal boundary, overflow, signed zero).
 """
@@ -59,6 +59,29 @@ def test_against_integer_rounding_of_f32_patterns():
     nan = np.isnan(x)
     assert np.array_equal(got[~nan], want[~nan])
     assert np.all(bf16.is_nan_bits(got[nan]))
+
+
+def _sweep_chunk(lo: int, n: int) -> int:
+    """Mismatches between the oracle and the integer form over float32
+    patterns lo .. lo + n - 1 (NaN patterns: the oracle must give a NaN)."""
+    u = np.arange(lo, lo + n, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32).astype(np.float64)
+    got = bf16.bits_from_f64(x)
+    want = _int_rne_f32(u)
+    nan = np.isnan(x)
+    bad = int(np.count_nonzero(got[~nan] != want[~nan]))
+    bad += int(np.count_nonzero(~bf16.is_nan_bits(got[nan])))
+    return bad
+
+
+def test_every_f32_pattern():
+    """All 2^32 float32 bit patterns, in chunks over the host's cores."""
+    from concurrent.futures import ProcessPoolExecutor
+    n = 1 << 24
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with ProcessPoolExecutor(max_workers=workers) as ex:
+        bad = sum(ex.map(_sweep_chunk, range(0, 1 << 32, n), [n] * (1 << 8)))
+    assert bad == 0
 
 
 def test_against_torch_conversion():
