@@ -14,7 +14,9 @@ prompt's matrix-heavy launches, and the same call 20 times back to back), and
 the CPU oracle timed on a bounded sample.
 Apart from the step: the 8192-token sliding-layer prompt (128-row chunks
 through a 1152-slot ring, window 1024, head dim 256, P rounded to bf16) in
-prompt tokens/s against the bf16 matrix-core peak; the one-row decode
+prompt tokens/s against the bf16 matrix-core peak, through attn_prefill_ws
+(each tile's key blocks split over four workgroups, then merged) and, for
+reference, attn_prefill; the one-row decode
 workloads of 512 keys, of 8 streams over a 1024-slot sliding ring and of 8
 streams over 32768 global-layer keys against HBM bandwidth (the two small
 ones also cold, rotating over K/V sets larger than the last-level cache);
@@ -137,14 +139,16 @@ def decode_windows(ga, torch, dev, iters: int = 10):
             "kv_GB/s": round(kv_bytes / (us * 1e-6) / 1e9, 1)}
 
 
-def prefill_sliding(ga, torch, dev, reps: int = 3):
+def prefill_sliding(ga, torch, dev, reps: int = 3, split: bool = True):
     """The 8192-token sliding-layer prompt: 64 chunks of 128 rows, each a
-    cache write into the 1152-slot ring then prompt attention over it.
-    Prompt tokens/s over the summed attention-kernel durations (HIP events
-    on the launch stream around each prefill launch) and over the whole
-    chunk sequence with its cache writes (a separate pass with no events
-    between launches); algorithmic flops 4 D per attended (row, key, query
-    head)."""
+    cache write into the 1152-slot ring then prompt attention over it
+    (split: attn_prefill_ws, whose 64-workgroup chunks split each tile's key
+    blocks over four workgroups and merge; else attn_prefill).  Prompt
+    tokens/s over the summed attention durations (HIP events on the launch
+    stream around each attention call, its merge launch included) and over
+    the whole chunk sequence with its cache writes (a separate pass with no
+    events between launches); algorithmic flops 4 D per attended (row, key,
+    query head)."""
     from synthetic.gen import WORKLOADS
     w = WORKLOADS["prefill_sliding_8k"]
     n, ch, Hq, Hkv, D = w.n_rows, w.chunk, w.Hq, w.Hkv, w.D
@@ -155,6 +159,8 @@ def prefill_sliding(ga, torch, dev, reps: int = 3):
     kc = torch.zeros((Hkv, w.cap, D), dtype=torch.bfloat16, device=dev)
     vc = torch.zeros_like(kc)
     out = torch.empty_like(q)
+    ws = (torch.empty(ga.attn_prefill_workspace_bytes(ch, Hq, D), dtype=torch.uint8, device=dev)
+          if split else None)
     starts = list(range(0, n, ch))
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in starts]
@@ -166,8 +172,8 @@ def prefill_sliding(ga, torch, dev, reps: int = 3):
             ga.attn_cache_write(kc, vc, k[r0:r0 + m], v[r0:r0 + m], r0, m, Hkv, D, w.cap, w.ring)
             if record:
                 ev[i][0].record()
-            ga.attn_prefill(out[r0:r0 + m], q[r0:r0 + m], kc, vc, r0, m, Hq, Hkv, D, w.cap,
-                            w.ring, w.window, w.scale, w.p_mode)
+            ga.attn_prefill_ws(out[r0:r0 + m], q[r0:r0 + m], kc, vc, r0, m, Hq, Hkv, D, w.cap,
+                               w.ring, w.window, w.scale, w.p_mode, ws)
             if record:
                 ev[i][1].record()
     prompt(False)
@@ -188,7 +194,8 @@ def prefill_sliding(ga, torch, dev, reps: int = 3):
     wms = sorted(wall_ms)[reps // 2]
     flops = causal_pairs(n, w.window) * Hq * 4 * D
     tf = flops / (kms * 1e-3) / 1e12
-    return {"workload": w.name, "prompt_tokens": n, "chunk_rows": ch, "ring_slots": w.cap,
+    return {"workload": w.name, "entry_point": "attn_prefill_ws" if split else "attn_prefill",
+            "prompt_tokens": n, "chunk_rows": ch, "ring_slots": w.cap,
             "window": w.window, "head_dim": D, "q_heads": Hq, "kv_heads": Hkv, "p_mode": "bf16",
             "kernel_ms": round(kms, 3), "tokens_per_s_kernels": round(n / (kms * 1e-3), 1),
             "wall_ms_with_cache_writes": round(wms, 3),
@@ -647,6 +654,10 @@ def main():
     del q, k, v, kc, vc, out, dk, dv
     torch.cuda.empty_cache()
     rec["prefill_sliding_8k"] = prefill_sliding(ga, torch, dev)
+    plain = prefill_sliding(ga, torch, dev, split=False)
+    rec["prefill_sliding_8k"]["attn_prefill_unsplit"] = {
+        k: plain[k] for k in ("kernel_ms", "tokens_per_s_kernels", "wall_ms_with_cache_writes",
+                              "frac_bf16_peak")}
     rec["decode_configs"] = decode_configs(ga, torch, dev)
     rec["decode_configs_cold"] = decode_cold(ga, torch, dev)
     rec["decode_windows"] = decode_windows(ga, torch, dev)

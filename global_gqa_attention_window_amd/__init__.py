@@ -59,6 +59,11 @@ _lib.attn_decode_prep_fused.argtypes = ([_c_void_p] * 5 + [_c_float, _c_int] + [
                                                         _c_void_p])
 _lib.attn_prefill.restype = _c_int
 _lib.attn_prefill.argtypes = ([_c_void_p] * 4 + [_c_int] * 8 + [_c_float, _c_int, _c_void_p, _c_void_p])
+_lib.attn_prefill_workspace_bytes.restype = _c_size_t
+_lib.attn_prefill_workspace_bytes.argtypes = [_c_int] * 3
+_lib.attn_prefill_ws.restype = _c_int
+_lib.attn_prefill_ws.argtypes = ([_c_void_p] * 4 + [_c_int] * 8 +
+                                 [_c_float, _c_int, _c_void_p, _c_void_p, _c_size_t, _c_void_p])
 _lib.attn_cache_write.restype = _c_int
 _lib.attn_cache_write.argtypes = [_c_void_p] * 4 + [_c_int] * 6 + [_c_void_p]
 _lib.attn_prefill_key_block.restype = _c_int
@@ -254,6 +259,26 @@ def attn_prefill(out, q, k_cache, v_cache, pos0, n_rows, n_q_heads, n_kv_heads,
                            head_dim, cache_cap, ring, window, float(scale), p_mode,
                            _arg(last_key, "last_key", n_rows, 4), _stream(stream))
     _ok(st, "attn_prefill")
+
+
+def attn_prefill_workspace_bytes(n_rows, n_q_heads, head_dim) -> int:
+    return _lib.attn_prefill_workspace_bytes(n_rows, n_q_heads, head_dim)
+
+
+def attn_prefill_ws(out, q, k_cache, v_cache, pos0, n_rows, n_q_heads, n_kv_heads,
+                    head_dim, cache_cap, ring, window, scale, p_mode, workspace,
+                    last_key=None, stream=None) -> None:
+    """attn_prefill with a device workspace (uint8, attn_prefill_workspace_bytes
+    bytes; None gives attn_prefill): a short chunk's key blocks may split over
+    several workgroups, joined by a merge launch."""
+    nq, nc = n_rows * n_q_heads * head_dim, n_kv_heads * cache_cap * head_dim
+    ws, wsb = _ws(workspace, None)
+    st = _lib.attn_prefill_ws(_arg(out, "out", nq), _arg(q, "q", nq),
+                              _arg(k_cache, "k_cache", nc), _arg(v_cache, "v_cache", nc),
+                              pos0, n_rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring,
+                              window, float(scale), p_mode, _arg(last_key, "last_key", n_rows, 4),
+                              ws, wsb, _stream(stream))
+    _ok(st, "attn_prefill_ws")
 
 
 def attn_cache_write(k_cache, v_cache, k, v, pos0, n_rows, n_kv_heads, head_dim,

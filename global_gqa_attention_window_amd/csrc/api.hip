@@ -313,7 +313,43 @@ int attn_prefill(void* out, const void* q, const void* k_cache,
         static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
         static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
         pos0, n_rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring, window,
-        scale, p_mode, last_key, static_cast<hipStream_t>(stream));
+        scale, p_mode, last_key, nullptr, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
+size_t attn_prefill_workspace_bytes(int n_rows, int n_q_heads, int head_dim) {
+    if (n_rows < 0 || n_q_heads < 1 || (head_dim != 256 && head_dim != 512)) return 0;
+    // (bf16 count: twice as many entries gives the fp32 partials' bytes)
+    if (tensor_bytes(n_rows, n_q_heads, 2 * PREFILL_MAX_SPLIT, head_dim + 2) < 0) return 0;
+    return prefill_partials_bytes(n_rows, n_q_heads, head_dim, PREFILL_MAX_SPLIT);
+}
+
+int attn_prefill_ws(void* out, const void* q, const void* k_cache,
+                    const void* v_cache, int pos0, int n_rows, int n_q_heads,
+                    int n_kv_heads, int head_dim, int cache_cap, int ring,
+                    int window, float scale, int p_mode,
+                    const int32_t* last_key, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    if (workspace == nullptr)
+        return attn_prefill(out, q, k_cache, v_cache, pos0, n_rows, n_q_heads, n_kv_heads,
+                            head_dim, cache_cap, ring, window, scale, p_mode, last_key, stream);
+    const int st = check_prefill(pos0, n_rows, n_q_heads, n_kv_heads, head_dim, cache_cap,
+                                 ring, window, scale, p_mode);
+    if (st != ATTN_OK) return st;
+    if (n_rows == 0) return ATTN_OK;
+    if (!out || !q || !k_cache || !v_cache) return ATTN_E_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(workspace))
+        return ATTN_E_ALIGN;
+    if (last_key && (reinterpret_cast<uintptr_t>(last_key) & 3u)) return ATTN_E_ALIGN;
+    const size_t need = attn_prefill_workspace_bytes(n_rows, n_q_heads, head_dim);
+    if (need == 0) return ATTN_E_RANGE;
+    if (workspace_bytes < need) return ATTN_E_WORKSPACE;
+    hipError_t e = launch_prefill(
+        static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+        static_cast<const uint16_t*>(k_cache), static_cast<const uint16_t*>(v_cache),
+        pos0, n_rows, n_q_heads, n_kv_heads, head_dim, cache_cap, ring, window,
+        scale, p_mode, last_key, workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 

@@ -42,11 +42,22 @@ hipError_t launch_decode_counters_init(void* ws, hipStream_t stream);
 
 int prefill_key_block(int D, int p_mode);
 
+// split prompt attention (head dim 256): at most PREFILL_MAX_SPLIT
+// workgroups share a tile's key blocks; the count a launch uses, and the
+// bytes of partials it writes (one fp32 (max, sum, accumulator[D]) per
+// (row, query head, range))
+constexpr int PREFILL_MAX_SPLIT = 4;
+int prefill_split_count(int n_rows, int Hq, int Hkv, int D);
+size_t prefill_partials_bytes(int n_rows, int Hq, int D, int S);
+
+// ws: NULL for one workgroup a tile; else room for
+// prefill_partials_bytes(n_rows, Hq, D, PREFILL_MAX_SPLIT), and the launch
+// splits a tile's key blocks when few workgroups would fill the chip
 hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                           const uint16_t* vc, int pos0, int n_rows, int Hq,
                           int Hkv, int D, int cap, int ring, int window,
                           float scale, int p_mode, const int32_t* last_key,
-                          hipStream_t stream);
+                          void* ws, hipStream_t stream);
 
 // head dim 512 (prefill512.hip)
 hipError_t launch_prefill_512(uint16_t* out, const uint16_t* q, const uint16_t* kc,

@@ -36,7 +36,17 @@
 // Lane l always owns query row l % 16 (the S^T and O^T column), so the row's
 // maximum, rescale and sum stay in its four lanes (l, l^16, l^32, l^48).
 // Key blocks are KB keys aligned to absolute positions; the running maximum
-// moves once per block and p is rounded against it.  Key slots of a block
+// moves once per block and p is rounded against it.
+// Split form (SPLIT): when one workgroup per tile leaves most of the chip
+// idle (a short chunk of a sliding layer: 64 workgroups), S workgroups share
+// a tile's key blocks, split into S consecutive ranges.  Workgroup s > 0
+// first forms the scores of the blocks before its range (score products
+// only, K alone staged) to reach the running maximum those blocks leave, so
+// its p are rounded against exactly the maxima the unsplit walk uses; then it
+// walks its own range and leaves a partial (maximum, row sum, accumulator)
+// that a merge launch joins in range order.  The ranges are uneven
+// (the first longest), so that every workgroup's walk, score-only blocks
+// included, takes about the same time.  Key slots of a block
 // outside the tile's attended span [lo, hi] are fetched from a position
 // inside the span instead: their scores are masked, and their V rows are
 // finite, so they add exactly zero (a never-written row is never read).
@@ -79,13 +89,32 @@ __host__ __device__ constexpr int sm_plan_steps(int cap, int nstg) {
     return t;
 }
 
-template <int D, int PM>
+// First block of range s of S over a tile's n blocks: round(n F_s), F_s =
+// (1 - x^s) / (1 - x^S), x = SPLIT_XN / SPLIT_XD the cost of a score-only
+// block relative to a whole one subtracted from 1 (the ranges where every
+// workgroup's walk costs the same).
+// (measured on MI355X: a score-only block takes about 0.54 of a whole one)
+constexpr int SPLIT_XN = 6, SPLIT_XD = 13;
+ATTN_DEV int split_start(int n, int S, int s) {
+    if (s <= 0) return 0;
+    if (s >= S) return n;
+    long long xs = 1, ds = 1, xS = 1, dS = 1;
+    for (int i = 0; i < s; ++i) { xs *= SPLIT_XN; ds *= SPLIT_XD; }
+    for (int i = 0; i < S; ++i) { xS *= SPLIT_XN; dS *= SPLIT_XD; }
+    // F_s = (1 - xs/ds) / (1 - xS/dS) = (dS - xs dS / ds) / (dS - xS)
+    const long long num = dS - xs * (dS / ds);
+    const long long den = dS - xS;
+    return (int)((2 * n * num + den) / (2 * den));
+}
+
+template <int D, int PM, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                     int pos0, int n_rows, int Hq, int Hkv, int G, int HG, int cap,
                     int ring, int window, float c,
-                    const int32_t* __restrict__ last_key) {
+                    const int32_t* __restrict__ last_key, int S,
+                    float* __restrict__ part_acc, float* __restrict__ part_ml) {
     constexpr int KB = PrefillCfg<D>::KB;
     constexpr int KPADP = 16;                // K padding per row (pair at 256)
     constexpr int VPADP = 16;                // V padding per row (pair at 256)
@@ -118,12 +147,15 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     // L is renumbered to put each XCD on a contiguous range of tiles ordered
     // KV group, head group, row tile: the workgroups sharing one L2 then
     // stream the same K/V blocks at about the same time
+    // (SPLIT: the S workgroups of a tile are consecutive in that order)
     const int n_rt = (n_rows + 15) / 16;
-    const int nwg = n_rt * Hkv * HG;
+    const int nwg = n_rt * Hkv * HG * (SPLIT ? S : 1);
     const int L = blockIdx.x;
     const int lam = (nwg % 8 == 0) ? (L % 8) * (nwg / 8) + L / 8 : L;
-    const int rt = lam % n_rt;
-    const int gh = lam / n_rt;                       // g * HG + head group
+    const int sp = SPLIT ? lam % S : 0;              // range of the tile's blocks
+    const int lt = SPLIT ? lam / S : lam;
+    const int rt = lt % n_rt;
+    const int gh = lt / n_rt;                        // g * HG + head group
     const int r0 = rt * 16;
     const int g = gh / HG;
     const int hl = (gh % HG) * 4 + wave;
@@ -151,21 +183,13 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int hi_tile = __builtin_amdgcn_readfirstlane(hi_m);
     const int b_lo = lo_tile / KB;
     const int b_hi = hi_tile / KB;
-
-    // Q^T operand: lane holds Q[row col][head h][32 st + 8 grp .. +7]
-    u32x4 qreg[QST];
-    {
-        const uint16_t* qrow = q + ((size_t)(r0 + (row_ok ? col : 0)) * Hq + h) * D + 8 * grp;
-#pragma unroll
-        for (int st = 0; st < QST; ++st) {
-            u32x4 z = {0u, 0u, 0u, 0u};
-            qreg[st] = (row_ok && head_ok) ? ld16(qrow + 32 * st) : z;
-        }
-        // Q lives in AGPRs (the products read their B operand from there),
-        // which leaves the VGPRs to the accumulators and to the operand reads
-        // in flight; all loads are issued before the first move
-#pragma unroll
-        for (int st = 0; st < QST; ++st) asm volatile("" : "+a"(qreg[st]));
+    // this workgroup's blocks [b_beg, b_end] (all of them unless SPLIT; a
+    // split range may be empty)
+    int b_beg = b_lo, b_end = b_hi;
+    if constexpr (SPLIT) {
+        const int nb = b_hi - b_lo + 1;
+        b_beg = b_lo + split_start(nb, S, sp);
+        b_end = b_lo + split_start(nb, S, sp + 1) - 1;
     }
 
     const uint16_t* Kg = kc + (size_t)g * cap * D;
@@ -232,6 +256,39 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     };
     constexpr int DMA_EVERY = 4;                 // fenced steps between DMA issues
 
+    // The first K/V loads go out before Q's, so that the two latencies
+    // overlap: the first three K blocks of SPLIT's score-only walk (all four
+    // LDS stages take K there), else K(b_beg), V(b_beg) and K(b_beg + 1)
+    const bool pre = SPLIT && b_beg > b_lo && b_beg <= b_end;    // a score-only walk first
+    const bool walk = b_beg <= b_end;                            // (false: an empty range)
+    static_assert(VBLK == KBLK, "K and V stages alike");
+    auto kstage = [&](int i) -> uint16_t* { return i < 2 ? ks_lds[i] : vs_lds[i - 2]; };
+    if (pre) {
+        for (int i = 0; i < 3; ++i)
+            if (b_lo + i < b_beg) dma(Kg, kstage(i), lane_dst, b_lo + i);
+    } else if (walk) {
+        dma(Kg, ks_lds[0], lane_dst, b_beg);
+        dma(Vg, vs_lds[0], lane_dstv, b_beg);
+        if (b_beg < b_end) dma(Kg, ks_lds[1], lane_dst, b_beg + 1);
+    }
+
+    // Q^T operand: lane holds Q[row col][head h][32 st + 8 grp .. +7]
+    u32x4 qreg[QST];
+    {
+        const uint16_t* qrow = q + ((size_t)(r0 + (row_ok ? col : 0)) * Hq + h) * D + 8 * grp;
+#pragma unroll
+        for (int st = 0; st < QST; ++st) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            qreg[st] = (row_ok && head_ok) ? ld16(qrow + 32 * st) : z;
+        }
+        // Q lives in AGPRs (the products read their B operand from there),
+        // which leaves the VGPRs to the accumulators and to the operand reads
+        // in flight; all loads are issued before the first move
+#pragma unroll
+        for (int st = 0; st < QST; ++st) asm volatile("" : "+a"(qreg[st]));
+    }
+
+
     // L2 prefetch.  Each XCD fetches every K/V block from memory once, and
     // its workgroups, which walk the blocks in step, would all wait on that
     // miss; so the workgroups of an XCD share out block b + PF_AHEAD one
@@ -296,6 +353,23 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         const u32x2 x0 = lds_read_tr16(vl + vofs + 2 * k2 * V16 + 16 * dt);
         const u32x2 x1 = lds_read_tr16(vl + vofs + (2 * k2 + 1) * V16 + 16 * dt);
         return u32x4{x0.x, x0.y, x1.x, x1.y};
+    };
+
+    // Scores alone (SPLIT's walk to its range): the score phase's products in
+    // its order, so every score has the same bits
+    auto score_only = [&](const uint16_t* kl, f32x4 (&sacc)[KT]) {
+        u32x4 kb[KPF];
+#pragma unroll
+        for (int j = 0; j < KPF; ++j) kb[j] = rd_k(kl, j);
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            sacc[j % KT] = mfma_bf16_16x16x32(kb[j % KPF], qreg[j / KT], sacc[j % KT]);
+            if (j + KPF < NS) kb[j % KPF] = rd_k(kl, j + KPF);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     // Score phase of a block: S^T from K stage kl into sacc (lane: keys
@@ -487,25 +561,61 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     }
     u32x4 vb[VPF];
 
-    // prologue: K(b_lo), V(b_lo) and K(b_lo + 1) in flight; softmax of b_lo
-    dma(Kg, ks_lds[0], lane_dst, b_lo);
-    dma(Vg, vs_lds[0], lane_dstv, b_lo);
-    if (b_lo < b_hi) dma(Kg, ks_lds[1], lane_dst, b_lo + 1);
+    // SPLIT: the running maximum the blocks before this range leave (their
+    // masked scores' maxima, times c, as the softmax takes them), K alone
+    // staged, the next block's K in flight beside each block's products
+    // (all four LDS stages take K here, three blocks in flight behind the
+    // one being scored)
+    if constexpr (SPLIT) {
+        if (pre) {
+            for (int b = b_lo; b < b_beg; ++b) {
+                const int st = (b - b_lo) & 3;
+                // K(b), this wave's share (blocks b + 1, b + 2 may be in flight)
+                if (b + 2 < b_beg) wait_vmcnt<2 * IPW>();
+                else if (b + 1 < b_beg) wait_vmcnt<IPW>();
+                else __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();                     // everyone's; K(b - 1) read
+                if (b + 3 < b_beg) dma(Kg, kstage((st + 3) & 3), lane_dst, b + 3);
+                if (head_ok) {
+                    f32x4 sacc[KT];
+                    score_only(kstage(st), sacc);
+                    if (!is_interior(b)) mask(b, sacc);
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kt][i]);
+                    mx = xmax4(mx);
+                    m_run = fmaxf(m_run, mx * c);
+                }
+            }
+            __syncthreads();                         // the last K stage read
+        }
+    }
+    // prologue: K(b_beg), V(b_beg) and K(b_beg + 1) in flight (issued at the
+    // start unless a score-only walk came first); softmax of b_beg
+    if (walk) {
+    if (pre) {
+        dma(Kg, ks_lds[0], lane_dst, b_beg);
+        dma(Vg, vs_lds[0], lane_dstv, b_beg);
+        if (b_beg < b_end) dma(Kg, ks_lds[1], lane_dst, b_beg + 1);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (head_ok) {
         f32x4 sacc[KT];
         score_phase(ks_lds[0], vs_lds[0], sacc, vb, 1.f, [](int) {});
-        if (!is_interior(b_lo)) mask(b_lo, sacc);
+        if (!is_interior(b_beg)) mask(b_beg, sacc);
 #pragma unroll
         for (int i = 0; i < SM_STEPS; ++i) sm_step(i, sacc, pch, pcl);
     }
-    __syncthreads();                             // K(b_lo) read by every wave
+    __syncthreads();                             // K(b_beg) read by every wave
+    }
 
     // Iteration b: the scores of block b + 1 (with the rescale that block b
     // needs), then block b's P.V beside block b + 1's softmax.
-    for (int b = b_lo; b < b_hi; ++b) {
-        const int st = (b - b_lo) & 1;
+    for (int b = b_beg; b < b_end; ++b) {
+        const int st = (b - b_beg) & 1;
         // in LDS now: V(b) in vs[st], K(b + 1) in ks[st ^ 1]; P(b) in pch / pcl.
         // K(b + 2) goes to ks[st] and V(b + 1) to vs[st ^ 1] beside the score
         // products, one instruction of each every DMA_EVERY steps, so both
@@ -543,8 +653,8 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         __builtin_amdgcn_s_waitcnt(0);          // this wave's DMAs of K(b+2), V(b+1)
         __syncthreads();                         // everyone's; K(b+1), V(b) free
     }
-    if (head_ok) {
-        const uint16_t* vl = vs_lds[(b_hi - b_lo) & 1];
+    if (head_ok && walk) {
+        const uint16_t* vl = vs_lds[(b_end - b_beg) & 1];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) oacc[dt] *= sm_alpha;
 #pragma unroll
@@ -558,6 +668,18 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 
     const float l_tot = xsum4(l_run);
     if (!(row_ok && head_ok)) return;
+    if constexpr (SPLIT) {
+        // the range's partial: (m, l) and the accumulator, for the merge
+        const size_t pidx = ((size_t)(r0 + col) * Hq + h) * S + sp;
+        if (grp == 0) {
+            part_ml[2 * pidx + 0] = m_run;
+            part_ml[2 * pidx + 1] = l_tot;
+        }
+        float* dst = part_acc + pidx * D + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = oacc[dt];
+        return;
+    }
     uint16_t* orow = out + ((size_t)(r0 + col) * Hq + h) * D + 4 * grp;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
@@ -567,6 +689,40 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     }
 }
 
+// Merge of a split launch's S range partials, one lane per 4 d of a (row,
+// head): M = the largest range maximum; range s weighted by 2^(m_s - M) (0
+// for a range with no attended key), acc and l summed in range order with one
+// rounding each (fmaf); out = bf16(acc / l).
+template <int D>
+__global__ __launch_bounds__(256)
+void prefill_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ part_acc,
+                          const float* __restrict__ part_ml, int n_rh, int S) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long rh = i / (D / 4);
+    if (rh >= n_rh) return;
+    const int d = (int)(i % (D / 4)) * 4;
+    const float* ml = part_ml + 2 * rh * S;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float l = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < S; ++s) {
+            const float m = ml[2 * s];
+            if (m == -INFINITY) continue;
+            const float w = fast_exp2(m - M);
+            const f32x4 a = *reinterpret_cast<const f32x4*>(part_acc + (rh * S + s) * D + d);
+            l = fmaf(w, ml[2 * s + 1], l);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = fmaf(w, a[k], acc[k]);
+        }
+    }
+    uint32_t b[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b[k] = (l != 0.f || l != l) ? f32_to_bf16_bits(acc[k] / l) : 0u;
+    *reinterpret_cast<u32x2*>(out + rh * D + d) = u32x2{pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+}
+
 }  // namespace
 
 int prefill_key_block(int D, int p_mode) {
@@ -574,23 +730,51 @@ int prefill_key_block(int D, int p_mode) {
     return D == 256 ? PrefillCfg<256>::KB : PrefillCfg<512>::KB;
 }
 
+int prefill_split_count(int n_rows, int Hq, int Hkv, int D) {
+    if (D != 256 || n_rows <= 0) return 1;
+    const long long base = (long long)((n_rows + 15) / 16) * Hkv * ((Hq / Hkv + 3) / 4);
+    // up to PREFILL_MAX_SPLIT workgroups a tile while the grid stays within
+    // one round of the chip (one workgroup a CU)
+    long long S = 256 / base;
+    return (int)(S < 1 ? 1 : (S > PREFILL_MAX_SPLIT ? PREFILL_MAX_SPLIT : S));
+}
+
+size_t prefill_partials_bytes(int n_rows, int Hq, int D, int S) {
+    return (size_t)n_rows * Hq * S * (D + 2) * sizeof(float);
+}
+
 hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                           const uint16_t* vc, int pos0, int n_rows, int Hq,
                           int Hkv, int D, int cap, int ring, int window,
                           float scale, int p_mode, const int32_t* last_key,
-                          hipStream_t stream) {
+                          void* ws, hipStream_t stream) {
     if (D == 512)
         return launch_prefill_512(out, q, kc, vc, pos0, n_rows, Hq, Hkv, cap, ring, window,
                                   scale, p_mode, last_key, stream);
     const int G = Hq / Hkv;
     const int HG = (G + 3) / 4;
     const float c = scale * ATTN_LOG2E;
-    dim3 grid(((n_rows + 15) / 16) * Hkv * HG);
-    if (p_mode == ATTN_P_BF16X2)
-        prefill_kernel<256, ATTN_P_BF16X2><<<grid, 256, 0, stream>>>(
-            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key);
-    else
-        prefill_kernel<256, ATTN_P_BF16><<<grid, 256, 0, stream>>>(
-            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key);
+    const int S = ws ? prefill_split_count(n_rows, Hq, Hkv, D) : 1;
+    dim3 grid(((n_rows + 15) / 16) * Hkv * HG * S);
+    float* part_acc = static_cast<float*>(ws);
+    float* part_ml = S > 1 ? part_acc + (size_t)n_rows * Hq * S * D : nullptr;
+#define PF_LAUNCH(PP, SP)                                                                     \
+    prefill_kernel<256, PP, SP><<<grid, 256, 0, stream>>>(                                    \
+        out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key, S,      \
+        part_acc, part_ml)
+    if (S > 1) {
+        if (p_mode == ATTN_P_BF16X2) PF_LAUNCH(ATTN_P_BF16X2, true);
+        else PF_LAUNCH(ATTN_P_BF16, true);
+    } else {
+        if (p_mode == ATTN_P_BF16X2) PF_LAUNCH(ATTN_P_BF16X2, false);
+        else PF_LAUNCH(ATTN_P_BF16, false);
+    }
+#undef PF_LAUNCH
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || S == 1) return e;
+    const long long n_rh = (long long)n_rows * Hq;
+    const long long threads = n_rh * (256 / 4);
+    prefill_merge_kernel<256><<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(
+        out, part_acc, part_ml, (int)n_rh, S);
     return hipGetLastError();
 }

@@ -334,6 +334,39 @@ int attn_prefill(void* out, const void* q, const void* k_cache,
                  int window, float scale, int p_mode,
                  const int32_t* last_key, void* stream);
 
+/* Bytes of device workspace attn_prefill_ws may use for n_rows rows of
+   n_q_heads heads (partials of up to four key ranges per row and head); 0
+   for arguments it would refuse. */
+size_t attn_prefill_workspace_bytes(int n_rows, int n_q_heads, int head_dim);
+
+/*
+ * attn_prefill with a workspace, for launches that one workgroup per
+ * 16-row tile would leave mostly idle (a 128-row chunk of a sliding layer
+ * takes 64 workgroups on a 256-CU chip).  At head dim 256 the library then
+ * splits each tile's key blocks into up to four consecutive ranges on
+ * workgroups of their own; a range after the first first forms the scores of
+ * the blocks before it, so that its running maxima, and with them every
+ * rounded P, equal the unsplit walk's (PR #975 prompt attention commits: the
+ * maximum moves once a block, p rounded against it); each range leaves a
+ * partial (maximum, row sum, accumulator) and a merge launch joins them in
+ * range order, as decode joins its chunk partials (PR #1183 window_rows
+ * notes).  Outputs
+ * differ from attn_prefill's only by the order of fp32 additions.  The split
+ * count depends on n_rows, Hq and Hkv alone.  At head dim 512, or with a NULL
+ * workspace, this is attn_prefill.
+ *
+ *   workspace        device, 16-byte aligned, >= attn_prefill_workspace_bytes
+ *                    (n_rows, Hq, D) bytes (else ATTN_E_WORKSPACE); contents
+ *                    on entry are ignored; calls sharing one must not overlap
+ *   (the rest as attn_prefill)
+ */
+int attn_prefill_ws(void* out, const void* q, const void* k_cache,
+                    const void* v_cache, int pos0, int n_rows, int n_q_heads,
+                    int n_kv_heads, int head_dim, int cache_cap, int ring,
+                    int window, float scale, int p_mode,
+                    const int32_t* last_key, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /*
  * Write a chunk's new keys and values into the cache before attention
  * (PR #975, the cache-before-attention commit): row r goes to the slot of

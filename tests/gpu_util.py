@@ -53,10 +53,11 @@ def run_decode_rows(ga, q, k, v, pos, Hkv, ring, window, scale):
 
 
 def run_prefill(ga, q, k, v, Hkv, cap, ring, window, scale, p_mode, chunk,
-                pos0=0, caches=None, last_key=None, starts=None):
+                pos0=0, caches=None, last_key=None, starts=None, split=False):
     """Prompt rows pos0.. in chunks: cache write, then attention, per chunk.
     Chunks of `chunk` rows, or starting at `starts` (row indices) when given.
-    last_key [n] (absolute positions, optional) is passed per chunk as given."""
+    last_key [n] (absolute positions, optional) is passed per chunk as given.
+    split: attention through attn_prefill_ws with a workspace."""
     n, Hq, D = q.shape
     if caches is None:
         kc = torch.zeros((Hkv, cap, D), dtype=torch.int16, device=DEV)
@@ -67,11 +68,20 @@ def run_prefill(ga, q, k, v, Hkv, cap, ring, window, scale, p_mode, chunk,
     out = torch.empty((n, Hq, D), dtype=torch.int16, device=DEV)
     lkd = None if last_key is None else up(np.asarray(last_key, dtype=np.int32))
     starts = list(range(0, n, chunk)) if starts is None else list(starts)
+    ws = None
+    if split:
+        longest = max(b - a for a, b in zip(starts, starts[1:] + [n]))
+        ws = torch.empty(ga.attn_prefill_workspace_bytes(longest, Hq, D), dtype=torch.uint8,
+                         device=DEV)
     for r0, r1 in zip(starts, starts[1:] + [n]):
         m = r1 - r0
         ga.attn_cache_write(kc, vc, kd[r0:r0 + m], vd[r0:r0 + m], pos0 + r0, m, Hkv, D,
                             cap, ring)
-        ga.attn_prefill(out[r0:r0 + m], qd[r0:r0 + m], kc, vc, pos0 + r0, m, Hq, Hkv, D,
-                        cap, ring, window, scale, p_mode,
-                        last_key=None if lkd is None else lkd[r0:r0 + m])
+        lk = None if lkd is None else lkd[r0:r0 + m]
+        if split:
+            ga.attn_prefill_ws(out[r0:r0 + m], qd[r0:r0 + m], kc, vc, pos0 + r0, m, Hq, Hkv,
+                               D, cap, ring, window, scale, p_mode, ws, last_key=lk)
+        else:
+            ga.attn_prefill(out[r0:r0 + m], qd[r0:r0 + m], kc, vc, pos0 + r0, m, Hq, Hkv, D,
+                            cap, ring, window, scale, p_mode, last_key=lk)
     return down(out), (kc, vc)

@@ -188,6 +188,41 @@ def test_prefill_edges_accepted_by_checks(ga):
     assert _prefill(ga, ring=0, window=0, cap=1000, pos0=872, n=0) == 0
 
 
+def _prefill_ws(ga, ws=P, ws_bytes=1 << 30, **kw):
+    a = dict(out=P, q=P, k=P, v=P, pos0=0, n=128, Hq=32, Hkv=4, D=256, cap=1152, ring=1,
+             window=1024, scale=0.0625, p_mode=P_BF16, last=None)
+    a.update(kw)
+    return ga._lib.attn_prefill_ws(a["out"], a["q"], a["k"], a["v"], a["pos0"], a["n"],
+                                   a["Hq"], a["Hkv"], a["D"], a["cap"], a["ring"], a["window"],
+                                   a["scale"], a["p_mode"], a["last"], ws, ws_bytes, None)
+
+
+def test_prefill_workspace_bytes(ga):
+    # fp32 (max, sum, accumulator[D]) for up to four key ranges per row and head
+    assert ga.attn_prefill_workspace_bytes(128, 32, 256) == 128 * 32 * 4 * 258 * 4
+    assert ga.attn_prefill_workspace_bytes(0, 32, 256) == 0
+    assert ga.attn_prefill_workspace_bytes(128, 32, 384) == 0
+    assert ga.attn_prefill_workspace_bytes(-1, 32, 256) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ws_bytes=100), "ATTN_E_WORKSPACE"), (dict(ws=P + 8), "ATTN_E_ALIGN"),
+    (dict(out=None), "ATTN_E_NULL"), (dict(D=64), "ATTN_E_HEAD_DIM"),
+    (dict(p_mode=P_FP32), "ATTN_E_P_MODE"), (dict(cap=1150), "ATTN_E_CACHE"),
+    (dict(pos0=-5), "ATTN_E_RANGE"), (dict(last=P + 2), "ATTN_E_ALIGN"),
+    # a NULL workspace takes attn_prefill's path and checks
+    (dict(ws=None, q=None), "ATTN_E_NULL"), (dict(ws=None, window=-1), "ATTN_E_WINDOW"),
+])
+@no_gpu
+def test_prefill_ws_refusals(ga, kw, status):
+    assert _prefill_ws(ga, **kw) == _status(status)
+
+
+@no_gpu
+def test_prefill_ws_zero_rows_is_a_no_op(ga):
+    assert _prefill_ws(ga, n=0, out=None, ws_bytes=0) == 0
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(kc=None), "ATTN_E_NULL"), (dict(v=None), "ATTN_E_NULL"),
     (dict(D=100), "ATTN_E_HEAD_DIM"), (dict(Hkv=0), "ATTN_E_GQA"),
