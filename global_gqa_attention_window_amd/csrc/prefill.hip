@@ -702,19 +702,29 @@ void prefill_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ 
     if (rh >= n_rh) return;
     const int d = (int)(i % (D / 4)) * 4;
     const float* ml = part_ml + 2 * rh * S;
+    // every range's loads go out before any is used (S <= PREFILL_MAX_SPLIT;
+    // a range past S repeats the last, weighted 0)
+    float2 mlv[PREFILL_MAX_SPLIT];
+    f32x4 av[PREFILL_MAX_SPLIT];
+#pragma unroll
+    for (int s = 0; s < PREFILL_MAX_SPLIT; ++s) {
+        const int sc = min(s, S - 1);
+        mlv[s] = *reinterpret_cast<const float2*>(ml + 2 * sc);
+        av[s] = *reinterpret_cast<const f32x4*>(part_acc + (rh * S + sc) * D + d);
+    }
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+    for (int s = 0; s < PREFILL_MAX_SPLIT; ++s) M = fmaxf(M, mlv[s].x);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float l = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < S; ++s) {
-            const float m = ml[2 * s];
-            if (m == -INFINITY) continue;
-            const float w = fast_exp2(m - M);
-            const f32x4 a = *reinterpret_cast<const f32x4*>(part_acc + (rh * S + s) * D + d);
-            l = fmaf(w, ml[2 * s + 1], l);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) acc[k] = fmaf(w, a[k], acc[k]);
+        for (int s = 0; s < PREFILL_MAX_SPLIT; ++s) {
+            if (s >= S || mlv[s].x == -INFINITY) continue;
+            const float w = fast_exp2(mlv[s].x - M);
+            l = fmaf(w, mlv[s].y, l);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[k] = fmaf(w, av[s][k], acc[k]);
         }
     }
     uint32_t b[4];
