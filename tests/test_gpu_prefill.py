@@ -3,9 +3,11 @@
 Prompt rows are fed chunk by chunk (cache write, then attention) exactly as
 the benchmark feeds them.  The full-size workloads run through the GPU once
 each: the 8k sliding prompt is checked on every output, the 32k global prompt
-on its whole last chunk (the longest key walk), a whole middle chunk and
-sampled rows (every head, every d of each), the oracle computing one row
-batch at a time; the small cases are checked on every output.
+on four whole chunks (the first, a quarter of the way in, the middle and the
+last, the longest key walk) and sampled rows (every head, every d of each),
+the oracle computing one row batch at a time, and on every output for the
+same bits under another chunking; the small cases are checked on every
+output.
 """
 import numpy as np
 import pytest
@@ -99,6 +101,31 @@ def test_prefill_global_32k_middle_chunk(global_32k, part):
     say("rows", rows[0], "..", rows[-1])
     _check(f"{w.name} middle chunk rows {rows[0]}..{rows[-1]}", got[rows],
            _oracle_rows(w, q, k, v, rows, 32))
+
+
+@pytest.mark.parametrize("first", [0, 8192])
+def test_prefill_global_32k_more_chunks(global_32k, first):
+    """Two more whole 512-row chunks: the first (rows 0..511, walks of up to
+    512 keys) and one a quarter of the way in, every head and d."""
+    w, q, k, v, got = global_32k
+    rows = np.arange(first, first + w.chunk)
+    say("rows", rows[0], "..", rows[-1])
+    _check(f"{w.name} chunk rows {rows[0]}..{rows[-1]}", got[rows],
+           _oracle_rows(w, q, k, v, rows, 32))
+
+
+def test_prefill_global_32k_every_row_chunking_invariant(ga, global_32k):
+    """Every row of the 32k prompt again through ragged chunks (1000 rows,
+    then a 777-row tail per 1777, none on a 512-row boundary): key blocks sit
+    on absolute positions, so all 32768 x 32 x 512 outputs keep their bits."""
+    w, q, k, v, got = global_32k
+    starts = sorted(set(range(0, w.n_rows, 1777)) | set(range(1000, w.n_rows, 1777)))
+    say("32k prompt re-chunked,", len(starts), "chunks")
+    again, _ = run_prefill(ga, q, k, v, w.Hkv, w.cap, w.ring, w.window, w.scale,
+                           w.p_mode, w.chunk, starts=starts)
+    diff = int(np.count_nonzero(again != got))
+    say("differing outputs", diff)
+    assert diff == 0
 
 
 @pytest.mark.parametrize("D,Hq,Hkv,ring,cap,window,chunk,n,pos0,p_mode", [
