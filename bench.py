@@ -302,6 +302,7 @@ def calib_lib():
     lib = ctypes.CDLL(path)
     lib.calib_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.calib_read_chunks.argtypes = lib.calib_read_stream.argtypes
     lib.calib_mfma_loop.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     lib.calib_clock.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     return lib
@@ -328,7 +329,8 @@ def gpu_clock_mhz(torch, dev):
 def attainable_kernels(torch, dev):
     """Measured ceilings of this part from kernels of our own: a read-only
     stream over 1 GiB (every byte read once with 16-byte loads over the whole
-    chip; the best of a few grid sizes and loads in flight) and a loop of bf16
+    chip, as a grid-stride walk or as contiguous per-workgroup shares with
+    nontemporal loads; the best of a few grid sizes and loads in flight) and a loop of bf16
     16x16x32 matrix products from registers, two waves on every SIMD (16384
     flops each); the shader clock measured right after each."""
     lib = calib_lib()
@@ -341,25 +343,28 @@ def attainable_kernels(torch, dev):
     src.fill_(1)
     sink = torch.empty(8192 * 256, dtype=torch.int32, device=dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best = None
-    for grid, unroll in ((2048, 8), (2048, 16), (4096, 4), (4096, 8), (8192, 4)):
+    best, rates = None, {}
+    for fn, grid, unroll in (("stride", 512, 8), ("stride", 2048, 8), ("stride", 4096, 4),
+                             ("chunks_nt", 256, 16), ("chunks_nt", 512, 8),
+                             ("chunks_nt", 1024, 8)):
+        f = lib.calib_read_stream if fn == "stride" else lib.calib_read_chunks
         for _ in range(2):
-            assert lib.calib_read_stream(src.data_ptr(), n, sink.data_ptr(), grid, unroll,
-                                         stream) == 0
+            assert f(src.data_ptr(), n, sink.data_ptr(), grid, unroll, stream) == 0
         torch.cuda.synchronize()
         reps = 10
         e0.record()
         for _ in range(reps):
-            lib.calib_read_stream(src.data_ptr(), n, sink.data_ptr(), grid, unroll, stream)
+            f(src.data_ptr(), n, sink.data_ptr(), grid, unroll, stream)
         e1.record()
         torch.cuda.synchronize()
         gbs = n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        rates[f"{fn} grid {grid} x{unroll}"] = round(gbs, 1)
         if best is None or gbs > best[0]:
-            best = (gbs, grid, unroll)
-    gbs, grid, unroll = best
+            best = (gbs, fn, grid, unroll)
+    gbs, fn, grid, unroll = best
     res["read_stream"] = {"GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                          "bytes": n, "grid": grid, "loads_in_flight": unroll,
-                          "clock_MHz_after": gpu_clock_mhz(torch, dev)}
+                          "bytes": n, "pattern": fn, "grid": grid, "loads_in_flight": unroll,
+                          "all_GB/s": rates, "clock_MHz_after": gpu_clock_mhz(torch, dev)}
     del src, sink
     grid, iters = 512, 40000
     sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)

@@ -6,6 +6,9 @@
 //                       a grid-stride walk over the whole chip; each thread
 //                       folds what it read into one word, written out so the
 //                       loads cannot be dropped
+//   calib_read_chunks   the same read with each workgroup walking a
+//                       contiguous share of the buffer, loads nontemporal
+//                       (streamed past the caches)
 //   calib_mfma_loop     waves that issue only v_mfma_f32_16x16x32_bf16 from
 //                       register operands (eight independent accumulators),
 //                       two waves per SIMD on every CU
@@ -41,6 +44,24 @@ __global__ __launch_bounds__(256) void read_stream_kernel(const u32x4* __restric
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
     sink[tid] = acc;
+}
+
+// each workgroup reads its contiguous share (n16 / grid words, a multiple
+// of 256 U) with nontemporal loads, U in flight per thread
+template <int U>
+__global__ __launch_bounds__(256) void read_chunks_kernel(const u32x4* __restrict__ src,
+                                                          size_t n16, uint32_t* __restrict__ sink) {
+    const size_t per = n16 / gridDim.x;
+    const u32x4* p = src + (size_t)blockIdx.x * per;
+    uint32_t acc = 0;
+    for (size_t i = threadIdx.x; i + (U - 1) * 256 < per; i += 256 * U) {
+        u32x4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(p + i + (size_t)u * 256);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
+    }
+    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
 // shader clock against the 100 MHz real-time counter over a matrix-core
@@ -103,6 +124,23 @@ int calib_read_stream(const void* src, size_t n_bytes, void* sink, int grid, int
     if (unroll == 16) read_stream_kernel<16><<<grid, 256, 0, st>>>(p, n_bytes / 16, k);
     else if (unroll == 8) read_stream_kernel<8><<<grid, 256, 0, st>>>(p, n_bytes / 16, k);
     else read_stream_kernel<4><<<grid, 256, 0, st>>>(p, n_bytes / 16, k);
+    return (int)hipGetLastError();
+}
+
+// Reads n_bytes at src once, workgroup b its contiguous share, nontemporal;
+// n_bytes must be a multiple of grid * 256 * 16 * unroll (8 or 16); sink
+// holds grid * 256 words.  Returns a hipError_t (hipErrorInvalidValue for a
+// size that does not split so).
+int calib_read_chunks(const void* src, size_t n_bytes, void* sink, int grid, int unroll,
+                      void* stream) {
+    if (grid < 1 || (unroll != 8 && unroll != 16) ||
+        n_bytes % ((size_t)grid * 256 * 16 * unroll) != 0)
+        return (int)hipErrorInvalidValue;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const u32x4* p = static_cast<const u32x4*>(src);
+    uint32_t* k = static_cast<uint32_t*>(sink);
+    if (unroll == 16) read_chunks_kernel<16><<<grid, 256, 0, st>>>(p, n_bytes / 16, k);
+    else read_chunks_kernel<8><<<grid, 256, 0, st>>>(p, n_bytes / 16, k);
     return (int)hipGetLastError();
 }
 

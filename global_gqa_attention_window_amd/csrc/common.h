@@ -107,6 +107,23 @@ ATTN_DEV void dma16_asm_sbase(const void* base, uint32_t voff, uint32_t lds_byte
 #endif
 }
 
+// ... the same, nontemporal (nt: the lines are streamed, not kept for reuse),
+// for data a launch reads once
+ATTN_DEV void dma16_asm_sbase_nt(const void* base, uint32_t voff, uint32_t lds_byte) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint64_t b64 = (uint64_t)(uintptr_t)base;
+    const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b64 >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b64);
+    const uint32_t lu = __builtin_amdgcn_readfirstlane(lds_byte);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(voff), "s"(bu), "s"(lu) : "memory");
+#else
+    (void)base;
+    (void)voff;
+    (void)lds_byte;
+#endif
+}
+
 // Wait until at most N of this wave's vector memory loads are outstanding
 // (loads complete in issue order for the count), with no wait on LDS or
 // export counters: the N most recent global->LDS loads may stay in flight.

@@ -12,6 +12,8 @@
 // window width.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "prologue.h"
@@ -72,6 +74,9 @@ int decode_run_chunks(int cap) {
     return r < 1 ? 1 : (r > 8 ? 8 : r);
 }
 constexpr int WPAD = 16;       // LDS padding elements per row (per row pair at 256)
+// K/V bytes above which a launch streams its K/V loads past the caches: the
+// MI355X last-level (Infinity) cache holds 256 MiB
+constexpr long long DECODE_STREAM_BYTES = 256ll << 20;
 
 // Merge width: the merge kernel's waves per (row, head) and d slice; a
 // workgroup that merges in place mirrors its summation order.
@@ -85,7 +90,10 @@ constexpr int MW = 16;
 // row, normed and rotated in place, and the workgroup whose run holds the
 // row's slot first writes the row's normed, rotated key and its value there
 // (the functions of prologue.h, so the bits equal the standalone prologue).
-template <int D, int DS, bool FUSE, bool PREP>
+// NTL: K/V blocks loaded nontemporal (streamed past the caches), for
+// launches whose K/V span outgrows the last-level cache, so that nothing of
+// it would be there for a later read anyway.
+template <int D, int DS, bool FUSE, bool PREP, bool NTL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_rows_kernel(const uint16_t* __restrict__ q,
                         const uint16_t* __restrict__ kc,
@@ -277,7 +285,8 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         }
     };
     auto dma_one = [&](const uint16_t* base, uint16_t* stage, const uint32_t (&vo)[NIW], int k) {
-        dma16_asm_sbase(base, vo[k], lds_addr(stage + dma_dst[k]));
+        if constexpr (NTL) dma16_asm_sbase_nt(base, vo[k], lds_addr(stage + dma_dst[k]));
+        else dma16_asm_sbase(base, vo[k], lds_addr(stage + dma_dst[k]));
     };
     // a block every row of the workgroup attends whole needs no mask: all
     // its slots attended together, its positions (consecutive) within
@@ -948,8 +957,17 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
     float* part_ml = part_acc + (size_t)S * R * Hq * nrun * D;
     const float c = scale * ATTN_LOG2E;
     const PrepArgs pa = prep ? *prep : PrepArgs{};
+    // K/V bytes the launch can read: each stream's window (plus the rows
+    // below its last) or its whole cache, per KV head
+    const long long span = window > 0 ? std::min<long long>(cap, (long long)window + R - 1) : cap;
+    const bool ntl = (double)S * Hkv * span * D * 4.0 > (double)DECODE_STREAM_BYTES;
 #define ROWS_LAUNCH(DD, SS, FF, PP)                                                           \
-    decode_rows_kernel<DD, SS, FF, PP><<<(unsigned)nwg, 256, 0, stream>>>(                    \
+    do {                                                                                      \
+        if (ntl) ROWS_LAUNCH_NT(DD, SS, FF, PP, true);                                        \
+        else ROWS_LAUNCH_NT(DD, SS, FF, PP, false);                                           \
+    } while (0)
+#define ROWS_LAUNCH_NT(DD, SS, FF, PP, NN)                                                    \
+    decode_rows_kernel<DD, SS, FF, PP, NN><<<(unsigned)nwg, 256, 0, stream>>>(                \
         q, kc, vc, pos, part_acc, part_ml, out, counters, R, Hq, Hkv, G, RPT, NT, CG,         \
         (int)n_items, cap, nrun, cpr, ring, window, c, pa)
 #define ROWS_DS(DD, FF)                                                                       \
@@ -974,6 +992,7 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
     }
 #undef ROWS_DS
 #undef ROWS_LAUNCH
+#undef ROWS_LAUNCH_NT
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess || one) return e;
     return launch_decode_merge(out, part_acc, part_ml, S * R * Hq, D, nrun, stream);
