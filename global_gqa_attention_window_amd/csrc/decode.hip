@@ -62,16 +62,28 @@ constexpr int CHUNK = ATTN_DECODE_CHUNK;
 // row keeps its bits at any window width.
 constexpr int WKB = 32;        // keys per block (one P.V product)
 
-// Chunks per run: a workgroup carries one online softmax over a run of
-// consecutive chunks and leaves one partial for it.  Runs grow with the cache
+// Slots per run: a workgroup carries one online softmax over a run of
+// consecutive slots and leaves one partial for it.  Runs grow with the cache
 // (fewer partials to write and merge) up to eight chunks, so that a 262144-key
-// cache over two KV heads takes 256 workgroups, one round on the chip; the
-// length depends on the cache capacity alone, so a row's bits depend neither
-// on the number of streams nor on the window width.
-int decode_run_chunks(int cap) {
+// cache over two KV heads takes 256 workgroups, one round on the chip.  A
+// cache of at most four chunks (1024 slots) takes half chunks, and one of at
+// most two (512 slots) quarter chunks: its one-row decode is a few
+// workgroups' chains of blocks, which shorter runs spread over more
+// workgroups (8 streams over a 1024-slot ring: 13.5 against 15.4 us; one
+// stream over 512 slots: 9.4 against 13.4 us).  Windows of many rows,
+// already thousands of workgroups, would pay more partials for nothing; they
+// take larger rings.  The length depends on the cache capacity alone, so a
+// row's bits depend neither on the number of streams nor on the window width.
+int decode_run_slots(int cap) {
     const int nch = (cap + CHUNK - 1) / CHUNK;
+    if (nch <= 2) return CHUNK / 4;
+    if (nch <= 4) return CHUNK / 2;
     const int r = nch / 16;
-    return r < 1 ? 1 : (r > 8 ? 8 : r);
+    return CHUNK * (r < 1 ? 1 : (r > 8 ? 8 : r));
+}
+int decode_run_count(int cap) {
+    const int rs = decode_run_slots(cap);
+    return (cap + rs - 1) / rs;
 }
 constexpr int WPAD = 16;       // LDS padding elements per row (per row pair at 256)
 // K/V bytes above which a launch streams its K/V loads past the caches: the
@@ -104,7 +116,7 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
                         uint16_t* __restrict__ out,
                         uint32_t* __restrict__ counters,
                         int R, int Hq, int Hkv, int G, int RPT, int NT, int CG,
-                        int n_items, int cap, int nrun, int cpr, int ring, int window,
+                        int n_items, int cap, int nrun, int run_slots, int ring, int window,
                         float c, PrepArgs pa) {
     // Head dim 256: two block sets (KP).  A workgroup takes one column tile;
     // waves 0, 1 take the even blocks of the run and waves 2, 3 the odd ones,
@@ -188,8 +200,8 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         return (slot < cap) & (t >= 0) & (p >= 0) & (p <= t) & ((w <= 0) | (t - p < w));
     };
 
-    const int slot0 = run * cpr * CHUNK;
-    const int nslot = min(cpr * CHUNK, cap - slot0);
+    const int slot0 = run * run_slots;
+    const int nslot = min(run_slots, cap - slot0);
     const int nblk = (nslot + WKB - 1) / WKB;
     int bb_lo = 0x7FFFFFFF, bb_hi = -1;
     for (int b0 = 0; b0 < nblk; b0 += 8) {
@@ -887,14 +899,14 @@ void decode_merge_kernel(uint16_t* __restrict__ out,
 }  // namespace
 
 size_t decode_workspace_bytes(int S, int Hq, int D, int cap) {
+    // one partial per chunk, or per run where runs are shorter (half chunks)
     const size_t nch = ((size_t)cap + CHUNK - 1) / CHUNK;
-    return (size_t)S * Hq * nch * ((size_t)D + 2) * sizeof(float);
+    const size_t nrun = (size_t)decode_run_count(cap);
+    return (size_t)S * Hq * (nrun > nch ? nrun : nch) * ((size_t)D + 2) * sizeof(float);
 }
 
 size_t decode_partials_bytes(int S, int Hq, int D, int cap) {
-    const size_t nch = ((size_t)cap + CHUNK - 1) / CHUNK;
-    const size_t cpr = (size_t)decode_run_chunks(cap);
-    const size_t nrun = (nch + cpr - 1) / cpr;
+    const size_t nrun = (size_t)decode_run_count(cap);
     return (size_t)S * Hq * nrun * ((size_t)D + 2) * sizeof(float);
 }
 
@@ -942,9 +954,8 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
     const int DS = D == 256 ? 2 : (NT == 1 ? 4 : (NT == 2 ? 2 : 1));
     const int WC = D == 256 ? 1 : 4 / DS;
     const int CG = (NT + WC - 1) / WC;           // workgroups per item
-    const int nch = (cap + CHUNK - 1) / CHUNK;
-    const int cpr = decode_run_chunks(cap);
-    const int nrun = (nch + cpr - 1) / cpr;
+    const int run_slots = decode_run_slots(cap);
+    const int nrun = decode_run_count(cap);
     const long long n_items = (long long)nrun * Hkv * S;
     const long long nwg = (n_items + 7) / 8 * 8 * CG;
     if (nwg > 0x7FFFFFFFLL || (long long)S * R * Hq > 0x7FFFFFFFLL) return hipErrorInvalidValue;
@@ -969,7 +980,7 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
 #define ROWS_LAUNCH_NT(DD, SS, FF, PP, NN)                                                    \
     decode_rows_kernel<DD, SS, FF, PP, NN><<<(unsigned)nwg, 256, 0, stream>>>(                \
         q, kc, vc, pos, part_acc, part_ml, out, counters, R, Hq, Hkv, G, RPT, NT, CG,         \
-        (int)n_items, cap, nrun, cpr, ring, window, c, pa)
+        (int)n_items, cap, nrun, run_slots, ring, window, c, pa)
 #define ROWS_DS(DD, FF)                                                                       \
     do {                                                                                      \
         if (prep) ROWS_LAUNCH(DD, 4, FF, true);                                               \

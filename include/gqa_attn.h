@@ -85,7 +85,8 @@ enum {
 /*
  * Bytes of device workspace attn_decode needs: one fp32 partial
  * (max, sum, accumulator[D]) per (stream, query head, 256-slot chunk), the
- * scratch PR #975's decode notes size by the number of chunks.
+ * scratch PR #975's decode notes size by the number of chunks, or per run
+ * where runs are shorter than a chunk (caches of at most 1024 slots).
  * Returns 0 for arguments attn_decode would refuse.
  */
 size_t attn_decode_workspace_bytes(int n_seq, int n_q_heads, int head_dim,
@@ -95,7 +96,8 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_q_heads, int head_dim,
  * One decode row per stream (PR #1183 window_rows notes; PR #975 decode
  * attention commits).  For stream s and query head h, with t = pos[s]:
  * keys are the cache slots whose position is attended by a row at t; each
- * run c of consecutive 256-slot chunks (1 to 8 chunks, fixed by cap alone)
+ * run c of consecutive slots (1 to 8 256-slot chunks, or a half or quarter
+ * chunk in caches of at most 1024 or 512 slots: fixed by cap alone)
  * yields m_c (a reference maximum within 8 of the run's largest score, in
  * log2 units), l_c = sum 2^(s log2(e) - m_c) and acc_c = the same weights
  * times v (at head dim 256 the run's even and odd 32-slot blocks are summed
@@ -175,7 +177,7 @@ size_t attn_decode_rows_workspace_bytes(int n_seq, int rows, int n_q_heads,
  * once for the window, and every row keeps its bits at any window width;
  * PR #1183 engine note: windows of up to 16 rows a stream).  Each row is an
  * ordinary decode row of its position (causal, window W): the keys are the
- * cache slots it attends, split into runs of 256-slot chunks whose partials
+ * cache slots it attends, split into runs of slots (as attn_decode) whose partials
  * merge in ascending order over the largest run maximum.  Probabilities stay
  * fp32 (the P.V products take each p as three bf16 pieces whose sum is p
  * exactly).  A row's output depends neither on `rows` nor on n_seq nor on

@@ -68,10 +68,14 @@ def test_key_block_matches_contract(ga):
 
 
 def test_workspace_bytes(ga):
-    # one fp32 (max, sum, acc[D]) per (stream, query head, 256-slot chunk)
+    # one fp32 (max, sum, acc[D]) per (stream, query head, 256-slot chunk);
+    # caches of at most 1024 (512) slots run half (quarter) chunks, one
+    # partial each
     assert ga.attn_decode_workspace_bytes(8, 32, 512, 32768) == 8 * 32 * 128 * 514 * 4
-    assert ga.attn_decode_workspace_bytes(1, 8, 256, 512) == 1 * 8 * 2 * 258 * 4
-    assert ga.attn_decode_workspace_bytes(1, 8, 256, 300) == 1 * 8 * 2 * 258 * 4
+    assert ga.attn_decode_workspace_bytes(1, 8, 256, 512) == 1 * 8 * 8 * 258 * 4
+    assert ga.attn_decode_workspace_bytes(1, 8, 256, 300) == 1 * 8 * 5 * 258 * 4
+    assert ga.attn_decode_workspace_bytes(1, 8, 256, 1024) == 1 * 8 * 8 * 258 * 4
+    assert ga.attn_decode_workspace_bytes(1, 8, 256, 1025) == 1 * 8 * 5 * 258 * 4
     assert ga.attn_decode_workspace_bytes(1, 8, 128, 512) == 0
     assert ga.attn_decode_workspace_bytes(1, 8, 256, 0) == 0
     assert ga.attn_decode_workspace_bytes(-1, 8, 256, 10) == 0
