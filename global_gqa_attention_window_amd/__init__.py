@@ -64,6 +64,9 @@ _lib.attn_prefill_workspace_bytes.argtypes = [_c_int] * 3
 _lib.attn_prefill_ws.restype = _c_int
 _lib.attn_prefill_ws.argtypes = ([_c_void_p] * 4 + [_c_int] * 8 +
                                  [_c_float, _c_int, _c_void_p, _c_void_p, _c_size_t, _c_void_p])
+_lib.attn_prefill_prompt.restype = _c_int
+_lib.attn_prefill_prompt.argtypes = ([_c_void_p] * 6 + [_c_int] * 9 +
+                                     [_c_float, _c_int, _c_void_p, _c_void_p, _c_size_t, _c_void_p])
 _lib.attn_cache_write.restype = _c_int
 _lib.attn_cache_write.argtypes = [_c_void_p] * 4 + [_c_int] * 6 + [_c_void_p]
 _lib.attn_prefill_key_block.restype = _c_int
@@ -279,6 +282,24 @@ def attn_prefill_ws(out, q, k_cache, v_cache, pos0, n_rows, n_q_heads, n_kv_head
                               window, float(scale), p_mode, _arg(last_key, "last_key", n_rows, 4),
                               ws, wsb, _stream(stream))
     _ok(st, "attn_prefill_ws")
+
+
+def attn_prefill_prompt(out, q, k, v, k_cache, v_cache, pos0, n_rows, chunk, n_q_heads,
+                        n_kv_heads, head_dim, cache_cap, ring, window, scale, p_mode,
+                        workspace=None, last_key=None, stream=None) -> None:
+    """A whole prompt in chunks of `chunk` rows (cache write, then attention,
+    per chunk): out/q [n_rows][Hq][D], k/v [n_rows][Hkv][D], caches
+    [Hkv][cap][D] (bf16); workspace None or as attn_prefill_ws's for one chunk."""
+    nq, nk = n_rows * n_q_heads * head_dim, n_rows * n_kv_heads * head_dim
+    nc = n_kv_heads * cache_cap * head_dim
+    ws, wsb = _ws(workspace, None)
+    st = _lib.attn_prefill_prompt(_arg(out, "out", nq), _arg(q, "q", nq), _arg(k, "k", nk),
+                                  _arg(v, "v", nk), _arg(k_cache, "k_cache", nc),
+                                  _arg(v_cache, "v_cache", nc), pos0, n_rows, chunk, n_q_heads,
+                                  n_kv_heads, head_dim, cache_cap, ring, window, float(scale),
+                                  p_mode, _arg(last_key, "last_key", n_rows, 4), ws, wsb,
+                                  _stream(stream))
+    _ok(st, "attn_prefill_prompt")
 
 
 def attn_cache_write(k_cache, v_cache, k, v, pos0, n_rows, n_kv_heads, head_dim,

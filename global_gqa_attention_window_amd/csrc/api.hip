@@ -353,6 +353,44 @@ int attn_prefill_ws(void* out, const void* q, const void* k_cache,
     return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
+int attn_prefill_prompt(void* out, const void* q, const void* k, const void* v,
+                        void* k_cache, void* v_cache, int pos0, int n_rows, int chunk,
+                        int n_q_heads, int n_kv_heads, int head_dim, int cache_cap, int ring,
+                        int window, float scale, int p_mode, const int32_t* last_key,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (chunk < 1) return ATTN_E_RANGE;
+    // every chunk meets attn_prefill's checks if the first (longest) does and
+    // the whole prompt fits the positions and the linear cache
+    const int first = n_rows < chunk ? n_rows : chunk;
+    const int st = check_prefill(pos0, first, n_q_heads, n_kv_heads, head_dim, cache_cap,
+                                 ring, window, scale, p_mode);
+    if (st != ATTN_OK) return st;
+    if (n_rows < 0) return ATTN_E_RANGE;
+    if (!ring && (long long)pos0 + n_rows > cache_cap) return ATTN_E_CACHE;
+    if ((long long)pos0 + n_rows + 64 > 0x7FFFFFFFLL ||
+        tensor_bytes(n_rows, n_q_heads, 1, head_dim) < 0 ||
+        tensor_bytes(n_rows, n_kv_heads, 1, head_dim) < 0)
+        return ATTN_E_RANGE;
+    if (n_rows == 0) return ATTN_OK;
+    if (!out || !q || !k || !v || !k_cache || !v_cache) return ATTN_E_NULL;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+        !aligned16(k_cache) || !aligned16(v_cache) || (workspace && !aligned16(workspace)))
+        return ATTN_E_ALIGN;
+    if (last_key && (reinterpret_cast<uintptr_t>(last_key) & 3u)) return ATTN_E_ALIGN;
+    if (workspace) {
+        const size_t need = attn_prefill_workspace_bytes(first, n_q_heads, head_dim);
+        if (need == 0) return ATTN_E_RANGE;
+        if (workspace_bytes < need) return ATTN_E_WORKSPACE;
+    }
+    const hipError_t e = launch_prefill_prompt(
+        static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),
+        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), pos0, n_rows, chunk,
+        n_q_heads, n_kv_heads, head_dim, cache_cap, ring, window, scale, p_mode, last_key,
+        workspace, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
+}
+
 int attn_cache_write(void* k_cache, void* v_cache, const void* k,
                      const void* v, int pos0, int n_rows, int n_kv_heads,
                      int head_dim, int cache_cap, int ring, void* stream) {

@@ -5,7 +5,7 @@
 // Row r of the chunk (position pos0 + r) goes to slot pos0 + r of a linear
 // cache, or (pos0 + r) mod cap of a ring.  Pure 16-byte copies: one thread
 // moves eight bf16 of one (row, KV head), consecutive threads walk d, so each
-// wave reads and writes 1 KiB of contiguous memory.
+// wave reads and writes 1 KiB of contiguous memory (cache_write_unit).
 #include "common.h"
 #include "kernels.h"
 
@@ -16,20 +16,8 @@ void cache_write_kernel(uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
                         const uint16_t* __restrict__ k,
                         const uint16_t* __restrict__ v, int pos0, int n_rows,
                         int Hkv, int D, int cap, int ring) {
-    const int vec_per_row = D / 8;
-    const size_t total = (size_t)n_rows * Hkv * vec_per_row;
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total) return;
-    const int dv = (int)(i % vec_per_row);
-    const size_t rg = i / vec_per_row;
-    const int g = (int)(rg % Hkv);
-    const int r = (int)(rg / Hkv);
-    const long long p = (long long)pos0 + r;
-    const long long slot = ring ? p % cap : p;
-    const size_t src = rg * D + (size_t)dv * 8;
-    const size_t dst = ((size_t)g * cap + (size_t)slot) * D + (size_t)dv * 8;
-    st16(kc + dst, ld16(k + src));
-    st16(vc + dst, ld16(v + src));
+    cache_write_unit(kc, vc, k, v, pos0, n_rows, Hkv, D, cap, ring,
+                     (size_t)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 }  // namespace

@@ -237,6 +237,29 @@ ATTN_DEV float xsum4(float x) {
 ATTN_DEV u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 ATTN_DEV void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Cache write, unit i of n_rows * Hkv * D / 8: eight bf16 of one (row, KV
+// head) of k and of v into the row's slot (pos0 + row of a linear cache,
+// (pos0 + row) mod cap of a ring); consecutive units walk d, so a wave reads
+// and writes 1 KiB of contiguous memory.  Units past the end do nothing.
+ATTN_DEV void cache_write_unit(uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+                               const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                               int pos0, int n_rows, int Hkv, int D, int cap, int ring,
+                               size_t i) {
+    const int vec_per_row = D / 8;
+    const size_t total = (size_t)n_rows * Hkv * vec_per_row;
+    if (i >= total) return;
+    const int dv = (int)(i % vec_per_row);
+    const size_t rg = i / vec_per_row;
+    const int g = (int)(rg % Hkv);
+    const int r = (int)(rg / Hkv);
+    const long long p = (long long)pos0 + r;
+    const long long slot = ring ? p % cap : p;
+    const size_t src = rg * D + (size_t)dv * 8;
+    const size_t dst = ((size_t)g * cap + (size_t)slot) * D + (size_t)dv * 8;
+    st16(kc + dst, ld16(k + src));
+    st16(vc + dst, ld16(v + src));
+}
+
 // log2(e) as float: scores are scaled by scale * log2(e) and exponentiated
 // with exp2, so exp(scale * s - m) = exp2(scale * log2e * s - m').
 #define ATTN_LOG2E 1.4426950408889634f

@@ -59,6 +59,16 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                           float scale, int p_mode, const int32_t* last_key,
                           void* ws, hipStream_t stream);
 
+// A prompt of n_rows rows in chunks of `chunk`: each chunk's cache write, then
+// its attention (as launch_cache_write + launch_prefill per chunk, with the
+// same bits); a split chunk's merge shares a launch with the next chunk's
+// cache write.  ws as launch_prefill's, sized for one chunk.
+hipError_t launch_prefill_prompt(uint16_t* out, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, uint16_t* kc, uint16_t* vc, int pos0,
+                                 int n_rows, int chunk, int Hq, int Hkv, int D, int cap,
+                                 int ring, int window, float scale, int p_mode,
+                                 const int32_t* last_key, void* ws, hipStream_t stream);
+
 // head dim 512 (prefill512.hip)
 hipError_t launch_prefill_512(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                               const uint16_t* vc, int pos0, int n_rows, int Hq, int Hkv,

@@ -50,6 +50,8 @@
 // outside the tile's attended span [lo, hi] are fetched from a position
 // inside the span instead: their scores are masked, and their V rows are
 // finite, so they add exactly zero (a never-written row is never read).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -694,10 +696,9 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 // for a range with no attended key), acc and l summed in range order with one
 // rounding each (fmaf); out = bf16(acc / l).
 template <int D>
-__global__ __launch_bounds__(256)
-void prefill_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ part_acc,
-                          const float* __restrict__ part_ml, int n_rh, int S) {
-    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+ATTN_DEV void prefill_merge_unit(uint16_t* __restrict__ out, const float* __restrict__ part_acc,
+                                 const float* __restrict__ part_ml, int n_rh, int S,
+                                 long long i) {
     const long long rh = i / (D / 4);
     if (rh >= n_rh) return;
     const int d = (int)(i % (D / 4)) * 4;
@@ -733,6 +734,25 @@ void prefill_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ 
     *reinterpret_cast<u32x2*>(out + rh * D + d) = u32x2{pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
 }
 
+// The merge of a split launch's range partials (workgroups below n_merge_wg),
+// and with it, in a chunked prompt, the cache write of the next chunk (the
+// rest): two independent steps in one launch.  Chunk c's attention has finished, so the ring
+// slots the write takes are no longer read, and the merge reads no cache.
+template <int D>
+__global__ __launch_bounds__(256)
+void merge_write_kernel(uint16_t* __restrict__ out, const float* __restrict__ part_acc,
+                        const float* __restrict__ part_ml, int n_rh, int S, int n_merge_wg,
+                        uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+                        const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                        int pos0, int n_rows, int Hkv, int cap, int ring) {
+    const int b = blockIdx.x;
+    if (b < n_merge_wg)
+        prefill_merge_unit<D>(out, part_acc, part_ml, n_rh, S, (long long)b * 256 + threadIdx.x);
+    else
+        cache_write_unit(kc, vc, k, v, pos0, n_rows, Hkv, D, cap, ring,
+                         (size_t)(b - n_merge_wg) * 256 + threadIdx.x);
+}
+
 }  // namespace
 
 int prefill_key_block(int D, int p_mode) {
@@ -753,11 +773,23 @@ size_t prefill_partials_bytes(int n_rows, int Hq, int D, int S) {
     return (size_t)n_rows * Hq * S * (D + 2) * sizeof(float);
 }
 
-hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
-                          const uint16_t* vc, int pos0, int n_rows, int Hq,
-                          int Hkv, int D, int cap, int ring, int window,
-                          float scale, int p_mode, const int32_t* last_key,
-                          void* ws, hipStream_t stream) {
+namespace {
+
+// a split launch's partials, left for its merge
+struct PrefillParts {
+    int S = 1;
+    float* acc = nullptr;
+    float* ml = nullptr;
+};
+
+// The attention launch of one chunk; with S > 1 in parts, its merge is
+// still to come.
+hipError_t launch_prefill_attend(uint16_t* out, const uint16_t* q, const uint16_t* kc,
+                                 const uint16_t* vc, int pos0, int n_rows, int Hq, int Hkv,
+                                 int D, int cap, int ring, int window, float scale,
+                                 int p_mode, const int32_t* last_key, void* ws,
+                                 hipStream_t stream, PrefillParts& parts) {
+    parts = PrefillParts{};
     if (D == 512)
         return launch_prefill_512(out, q, kc, vc, pos0, n_rows, Hq, Hkv, cap, ring, window,
                                   scale, p_mode, last_key, stream);
@@ -780,11 +812,68 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
         else PF_LAUNCH(ATTN_P_BF16, false);
     }
 #undef PF_LAUNCH
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess || S == 1) return e;
-    const long long n_rh = (long long)n_rows * Hq;
-    const long long threads = n_rh * (256 / 4);
-    prefill_merge_kernel<256><<<(unsigned)((threads + 255) / 256), 256, 0, stream>>>(
-        out, part_acc, part_ml, (int)n_rh, S);
+    parts.S = S;
+    parts.acc = part_acc;
+    parts.ml = part_ml;
     return hipGetLastError();
+}
+
+// The merge of a split chunk (rows of out) and the cache write of the next
+// chunk's n_next rows, in one launch where both are due; either alone
+// otherwise, or nothing.
+hipError_t launch_merge_write(uint16_t* out, int n_rows, int Hq, const PrefillParts& parts,
+                              uint16_t* kc, uint16_t* vc, const uint16_t* k,
+                              const uint16_t* v, int pos_next, int n_next, int Hkv, int D,
+                              int cap, int ring, hipStream_t stream) {
+    const long long n_rh = (long long)n_rows * Hq;
+    const unsigned merge_wg = parts.S > 1 ? (unsigned)((n_rh * (256 / 4) + 255) / 256) : 0u;
+    const unsigned write_wg = (unsigned)(((size_t)n_next * Hkv * (D / 8) + 255) / 256);
+    if (merge_wg == 0 && write_wg == 0) return hipSuccess;
+    if (merge_wg == 0)
+        return launch_cache_write(kc, vc, k, v, pos_next, n_next, Hkv, D, cap, ring, stream);
+    // (splits happen at head dim 256 only)
+    merge_write_kernel<256><<<merge_wg + write_wg, 256, 0, stream>>>(
+        out, parts.acc, parts.ml, (int)n_rh, parts.S, (int)merge_wg, kc, vc, k, v, pos_next,
+        n_next, Hkv, cap, ring);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
+                          const uint16_t* vc, int pos0, int n_rows, int Hq,
+                          int Hkv, int D, int cap, int ring, int window,
+                          float scale, int p_mode, const int32_t* last_key,
+                          void* ws, hipStream_t stream) {
+    PrefillParts parts;
+    const hipError_t e = launch_prefill_attend(out, q, kc, vc, pos0, n_rows, Hq, Hkv, D, cap,
+                                               ring, window, scale, p_mode, last_key, ws,
+                                               stream, parts);
+    if (e != hipSuccess) return e;
+    return launch_merge_write(out, n_rows, Hq, parts, nullptr, nullptr, nullptr, nullptr, 0, 0,
+                              Hkv, D, cap, ring, stream);
+}
+
+hipError_t launch_prefill_prompt(uint16_t* out, const uint16_t* q, const uint16_t* k,
+                                 const uint16_t* v, uint16_t* kc, uint16_t* vc, int pos0,
+                                 int n_rows, int chunk, int Hq, int Hkv, int D, int cap,
+                                 int ring, int window, float scale, int p_mode,
+                                 const int32_t* last_key, void* ws, hipStream_t stream) {
+    hipError_t e = launch_cache_write(kc, vc, k, v, pos0, std::min(chunk, n_rows), Hkv, D, cap,
+                                      ring, stream);
+    for (int r0 = 0; e == hipSuccess && r0 < n_rows; r0 += chunk) {
+        const int m = std::min(chunk, n_rows - r0);
+        const int r1 = r0 + m;
+        const int m_next = std::min(chunk, n_rows - r1);
+        const size_t qo = (size_t)r0 * Hq * D;
+        PrefillParts parts;
+        e = launch_prefill_attend(out + qo, q + qo, kc, vc, pos0 + r0, m, Hq, Hkv, D, cap, ring,
+                                  window, scale, p_mode, last_key ? last_key + r0 : nullptr, ws,
+                                  stream, parts);
+        if (e != hipSuccess) break;
+        const size_t ko = (size_t)r1 * Hkv * D;
+        e = launch_merge_write(out + qo, m, Hq, parts, kc, vc, k + ko, v + ko, pos0 + r1,
+                               m_next, Hkv, D, cap, ring, stream);
+    }
+    return e;
 }

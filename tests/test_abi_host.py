@@ -227,6 +227,36 @@ def test_prefill_ws_zero_rows_is_a_no_op(ga):
     assert _prefill_ws(ga, n=0, out=None, ws_bytes=0) == 0
 
 
+def _prompt(ga, ws=P, ws_bytes=1 << 30, **kw):
+    a = dict(out=P, q=P, k=P, v=P, kc=P, vc=P, pos0=0, n=8192, chunk=128, Hq=32, Hkv=4, D=256,
+             cap=1152, ring=1, window=1024, scale=0.0625, p_mode=P_BF16, last=None)
+    a.update(kw)
+    return ga._lib.attn_prefill_prompt(a["out"], a["q"], a["k"], a["v"], a["kc"], a["vc"],
+                                       a["pos0"], a["n"], a["chunk"], a["Hq"], a["Hkv"], a["D"],
+                                       a["cap"], a["ring"], a["window"], a["scale"], a["p_mode"],
+                                       a["last"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(chunk=0), "ATTN_E_RANGE"), (dict(n=-1), "ATTN_E_RANGE"),
+    (dict(chunk=130), "ATTN_E_CACHE"),                 # ring: cap < W + chunk - 1
+    (dict(ring=0, window=0, cap=8000), "ATTN_E_CACHE"),  # linear: the prompt passes cap
+    (dict(ws_bytes=100), "ATTN_E_WORKSPACE"), (dict(ws=P + 8), "ATTN_E_ALIGN"),
+    (dict(k=None), "ATTN_E_NULL"), (dict(vc=None), "ATTN_E_NULL"),
+    (dict(v=P + 2), "ATTN_E_ALIGN"), (dict(last=P + 2), "ATTN_E_ALIGN"),
+    (dict(D=64), "ATTN_E_HEAD_DIM"), (dict(p_mode=P_FP32), "ATTN_E_P_MODE"),
+    (dict(pos0=0x7FFFFFFF - 8192), "ATTN_E_RANGE"),
+])
+@no_gpu
+def test_prefill_prompt_refusals(ga, kw, status):
+    assert _prompt(ga, **kw) == _status(status)
+
+
+@no_gpu
+def test_prefill_prompt_zero_rows_is_a_no_op(ga):
+    assert _prompt(ga, n=0, out=None, k=None, ws=None, ws_bytes=0) == 0
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(kc=None), "ATTN_E_NULL"), (dict(v=None), "ATTN_E_NULL"),
     (dict(D=100), "ATTN_E_HEAD_DIM"), (dict(Hkv=0), "ATTN_E_GQA"),
