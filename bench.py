@@ -227,10 +227,41 @@ def prefill_sliding(ga, torch, dev, reps: int = 3, split: bool = True):
     return res
 
 
+def graph_us(torch, calls, n_calls: int, reps: int = 5):
+    """Device time per call of `calls` (a function that enqueues n_calls
+    library calls on the current stream), replayed from a captured HIP graph:
+    the calls' launches run back to back with no host work between them (a
+    decode step replayed as a graph, as a serving loop runs it).  Median of
+    reps replays, events around each."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                # warm-up outside the capture
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t = []
+    for _ in range(reps):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1) * 1e3 / n_calls)
+    del g
+    return sorted(t)[reps // 2]
+
+
 def decode_configs(ga, torch, dev, iters: int = 20):
     """One-row decode workloads (512 keys; 8 streams over a 1024-slot sliding
     ring; 8 streams over 32768 global-layer keys): us per call from HIP
-    events over back-to-back calls, K/V bytes attended once per (stream, KV
+    events over back-to-back calls replayed from a captured graph (the
+    eager calls' time, which the Python binding's per-call checks bound for
+    the small ones, beside it), K/V bytes attended once per (stream, KV
     head) plus q and out.  The two smaller caches stay in the 256 MB
     last-level cache between calls (warm); the 32768-key one (1 GiB) does not."""
     from synthetic.gen import WORKLOADS
@@ -258,14 +289,20 @@ def decode_configs(ga, torch, dev, iters: int = 20):
             call()
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / iters
+        us_eager = e0.elapsed_time(e1) * 1e3 / iters
+
+        def calls():
+            for _ in range(iters):
+                call()
+        us = graph_us(torch, calls, iters)
         keys = sum(min(w.cap, p + 1) if w.window <= 0 else min(w.cap, p + 1, w.window)
                    for p in w.pos)
         nbytes = 2 * w.Hkv * keys * w.D * 2 + 2 * w.S * w.Hq * w.D * 2
         gbs = nbytes / (us * 1e-6) / 1e9
         res[name] = {"us": round(us, 2), "GB/s": round(gbs, 1),
                      "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
-                     "cache": "warm" if nbytes < (256 << 20) else "cold"}
+                     "cache": "warm" if nbytes < (256 << 20) else "cold",
+                     "timing": "graph replay", "us_eager": round(us_eager, 2)}
         del q, kc, vc, out, ws
     torch.cuda.empty_cache()
     return res
@@ -275,7 +312,8 @@ def decode_cold(ga, torch, dev, min_bytes: int = 600 << 20):
     """The two small one-row decode workloads with their K/V out of the
     last-level cache: calls rotate over distinct K/V sets totalling more than
     600 MB (over twice the 256 MB cache), so every call's K/V comes from
-    HBM; us per call (HIP events over one pass of the rotation)."""
+    HBM; us per call (HIP events over one pass of the rotation replayed from
+    a captured graph; the eager pass beside it)."""
     from synthetic.gen import WORKLOADS
     res = {}
     for name in ("decode_g8_d256_512", "decode_sliding_ring1024"):
@@ -303,13 +341,19 @@ def decode_cold(ga, torch, dev, min_bytes: int = 600 << 20):
             call(i)
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / n_sets
+        us_eager = e0.elapsed_time(e1) * 1e3 / n_sets
+
+        def calls():
+            for i in range(n_sets):
+                call(i)
+        us = graph_us(torch, calls, n_sets, reps=3)
         keys = sum(min(w.cap, p + 1, w.window) for p in w.pos)
         nbytes = 2 * w.Hkv * keys * w.D * 2 + 2 * w.S * w.Hq * w.D * 2
         gbs = nbytes / (us * 1e-6) / 1e9
         res[name] = {"us": round(us, 2), "GB/s": round(gbs, 1),
                      "frac_hbm": round(gbs / PEAK_HBM_GBS, 4), "kv_sets": n_sets,
-                     "rotated_MB": round(n_sets * per_set / 1e6, 1)}
+                     "rotated_MB": round(n_sets * per_set / 1e6, 1),
+                     "timing": "graph replay", "us_eager": round(us_eager, 2)}
         del q, kv, out, ws
     torch.cuda.empty_cache()
     return res
