@@ -148,9 +148,10 @@ def prefill_sliding(ga, torch, dev, reps: int = 3, split: bool = True):
     stream around each attention call, its merge launch included) and over
     the whole chunk sequence with its cache writes (a separate pass with no
     events between launches); with split, also the whole prompt through one
-    attn_prefill_prompt call (cache writes included; the library drives the
-    chunks, each split chunk's merge sharing a launch with the next chunk's
-    cache write).  Algorithmic flops 4 D per attended (row, key, query head)."""
+    attn_prefill_prompt call (the bits of the unsplit chunked path, cache
+    writes included: the prompt's attended keys copied to a linear span, one
+    attention launch over all rows, the last rows into the ring).  Algorithmic
+    flops 4 D per attended (row, key, query head)."""
     from synthetic.gen import WORKLOADS
     w = WORKLOADS["prefill_sliding_8k"]
     n, ch, Hq, Hkv, D = w.n_rows, w.chunk, w.Hq, w.Hkv, w.D
@@ -198,19 +199,13 @@ def prefill_sliding(ga, torch, dev, reps: int = 3, split: bool = True):
     tf = flops / (kms * 1e-3) / 1e12
     whole = None
     if split:
+        pws = torch.empty(ga.attn_prefill_prompt_workspace_bytes(0, n, Hkv, D, w.ring, w.window),
+                          dtype=torch.uint8, device=dev)
+
         def prompt_call():
             ga.attn_prefill_prompt(out, q, k, v, kc, vc, 0, n, ch, Hq, Hkv, D, w.cap, w.ring,
-                                   w.window, w.scale, w.p_mode, workspace=ws)
-        prompt_call()
-        torch.cuda.synchronize()
-        call_ms = []
-        for _ in range(reps):
-            e0.record()
-            prompt_call()
-            e1.record()
-            torch.cuda.synchronize()
-            call_ms.append(e0.elapsed_time(e1))
-        pms = sorted(call_ms)[reps // 2]
+                                   w.window, w.scale, w.p_mode, workspace=pws)
+        pms = call_ms(torch, prompt_call, reps)
         ptf = flops / (pms * 1e-3) / 1e12
         whole = {"ms": round(pms, 3), "tokens_per_s": round(n / (pms * 1e-3), 1),
                  "TFLOP/s": round(ptf, 1), "frac_bf16_peak": round(ptf / PEAK_BF16_TFLOPS, 4)}
@@ -225,6 +220,21 @@ def prefill_sliding(ga, torch, dev, reps: int = 3, split: bool = True):
     if whole is not None:
         res["attn_prefill_prompt_with_cache_writes"] = whole
     return res
+
+
+def call_ms(torch, fn, reps: int) -> float:
+    """Median ms of fn() (one warm-up call first), HIP events around each."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t = []
+    for _ in range(reps):
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1))
+    return sorted(t)[reps // 2]
 
 
 def graph_us(torch, calls, n_calls: int, reps: int = 5):
@@ -723,13 +733,26 @@ def main():
     rec["decode"].update({"us_back_to_back": round(rep_us, 2),
                           "GB/s_back_to_back": round(rep_gbs, 1),
                           "frac_hbm_back_to_back": round(rep_gbs / PEAK_HBM_GBS, 4)})
+    # the same prompt through one attn_prefill_prompt call (its bits; a linear
+    # cache takes every row first, then one attention launch)
+    rec["prefill"]["attn_prefill_prompt_ms"] = round(call_ms(
+        torch, lambda: ga.attn_prefill_prompt(out, q, k, v, kc, vc, 0, n, ch, Hq, Hkv, D, w.cap,
+                                              w.ring, w.window, w.scale, w.p_mode), 2), 3)
     del q, k, v, kc, vc, out, dk, dv
     torch.cuda.empty_cache()
-    rec["prefill_sliding_8k"] = prefill_sliding(ga, torch, dev)
+    split = prefill_sliding(ga, torch, dev)
     plain = prefill_sliding(ga, torch, dev, split=False)
-    rec["prefill_sliding_8k"]["attn_prefill_unsplit"] = {
-        k: plain[k] for k in ("kernel_ms", "tokens_per_s_kernels", "wall_ms_with_cache_writes",
-                              "frac_bf16_peak")}
+    keep = ("kernel_ms", "tokens_per_s_kernels", "wall_ms_with_cache_writes", "TFLOP/s",
+            "frac_bf16_peak", "launch_us")
+    whole = split.pop("attn_prefill_prompt_with_cache_writes")
+    rec["prefill_sliding_8k"] = {
+        **{k: split[k] for k in ("workload", "prompt_tokens", "chunk_rows", "ring_slots",
+                                 "window", "head_dim", "q_heads", "kv_heads", "p_mode")},
+        "entry_point": "attn_prefill_prompt", "timing": "one call, cache writes included",
+        **whole,
+        "per_chunk_attn_prefill_ws": {k: split[k] for k in keep},
+        "per_chunk_attn_prefill": {k: plain[k] for k in keep},
+    }
     rec["decode_configs"] = decode_configs(ga, torch, dev)
     rec["decode_configs_cold"] = decode_cold(ga, torch, dev)
     rec["decode_windows"] = decode_windows(ga, torch, dev)

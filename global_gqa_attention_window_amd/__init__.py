@@ -64,6 +64,8 @@ _lib.attn_prefill_workspace_bytes.argtypes = [_c_int] * 3
 _lib.attn_prefill_ws.restype = _c_int
 _lib.attn_prefill_ws.argtypes = ([_c_void_p] * 4 + [_c_int] * 8 +
                                  [_c_float, _c_int, _c_void_p, _c_void_p, _c_size_t, _c_void_p])
+_lib.attn_prefill_prompt_workspace_bytes.restype = _c_size_t
+_lib.attn_prefill_prompt_workspace_bytes.argtypes = [_c_int] * 6
 _lib.attn_prefill_prompt.restype = _c_int
 _lib.attn_prefill_prompt.argtypes = ([_c_void_p] * 6 + [_c_int] * 9 +
                                      [_c_float, _c_int, _c_void_p, _c_void_p, _c_size_t, _c_void_p])
@@ -284,12 +286,18 @@ def attn_prefill_ws(out, q, k_cache, v_cache, pos0, n_rows, n_q_heads, n_kv_head
     _ok(st, "attn_prefill_ws")
 
 
+def attn_prefill_prompt_workspace_bytes(pos0, n_rows, n_kv_heads, head_dim, ring, window) -> int:
+    return _lib.attn_prefill_prompt_workspace_bytes(pos0, n_rows, n_kv_heads, head_dim, ring,
+                                                    window)
+
+
 def attn_prefill_prompt(out, q, k, v, k_cache, v_cache, pos0, n_rows, chunk, n_q_heads,
                         n_kv_heads, head_dim, cache_cap, ring, window, scale, p_mode,
                         workspace=None, last_key=None, stream=None) -> None:
-    """A whole prompt in chunks of `chunk` rows (cache write, then attention,
-    per chunk): out/q [n_rows][Hq][D], k/v [n_rows][Hkv][D], caches
-    [Hkv][cap][D] (bf16); workspace None or as attn_prefill_ws's for one chunk."""
+    """A whole prompt with the bits of cache write + attention chunk by chunk
+    (`chunk` rows each), in one attention launch: out/q [n_rows][Hq][D], k/v
+    [n_rows][Hkv][D], caches [Hkv][cap][D] (bf16); workspace (uint8,
+    attn_prefill_prompt_workspace_bytes) for a ring, None for a linear cache."""
     nq, nk = n_rows * n_q_heads * head_dim, n_rows * n_kv_heads * head_dim
     nc = n_kv_heads * cache_cap * head_dim
     ws, wsb = _ws(workspace, None)

@@ -8,6 +8,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace {
@@ -353,6 +355,17 @@ int attn_prefill_ws(void* out, const void* q, const void* k_cache,
     return e == hipSuccess ? ATTN_OK : ATTN_E_LAUNCH;
 }
 
+size_t attn_prefill_prompt_workspace_bytes(int pos0, int n_rows, int n_kv_heads, int head_dim,
+                                           int ring, int window) {
+    if (pos0 < 0 || n_rows < 0 || n_kv_heads < 1 || (head_dim != 256 && head_dim != 512) ||
+        (ring != 0 && ring != 1) || window < 0 || (ring && window == 0))
+        return 0;
+    if ((long long)pos0 + n_rows + 64 > 0x7FFFFFFFLL) return 0;
+    const long long span = (long long)pos0 + n_rows - std::max(0, pos0 - window + 1);
+    if (ring && tensor_bytes(2 * n_kv_heads, 1, span, head_dim) < 0) return 0;
+    return prefill_prompt_stage_bytes(pos0, n_rows, n_kv_heads, head_dim, ring, window);
+}
+
 int attn_prefill_prompt(void* out, const void* q, const void* k, const void* v,
                         void* k_cache, void* v_cache, int pos0, int n_rows, int chunk,
                         int n_q_heads, int n_kv_heads, int head_dim, int cache_cap, int ring,
@@ -377,10 +390,14 @@ int attn_prefill_prompt(void* out, const void* q, const void* k, const void* v,
         !aligned16(k_cache) || !aligned16(v_cache) || (workspace && !aligned16(workspace)))
         return ATTN_E_ALIGN;
     if (last_key && (reinterpret_cast<uintptr_t>(last_key) & 3u)) return ATTN_E_ALIGN;
-    if (workspace) {
-        const size_t need = attn_prefill_workspace_bytes(first, n_q_heads, head_dim);
+    if (ring) {
+        // the attended span's linear copy: one head's slice in 32-bit offsets
+        const long long span = (long long)pos0 + n_rows - std::max(0, pos0 - window + 1);
+        if (span * head_dim * 2 >= (1LL << 32)) return ATTN_E_RANGE;
+        const size_t need = attn_prefill_prompt_workspace_bytes(pos0, n_rows, n_kv_heads,
+                                                                head_dim, ring, window);
         if (need == 0) return ATTN_E_RANGE;
-        if (workspace_bytes < need) return ATTN_E_WORKSPACE;
+        if (!workspace || workspace_bytes < need) return ATTN_E_WORKSPACE;
     }
     const hipError_t e = launch_prefill_prompt(
         static_cast<uint16_t*>(out), static_cast<const uint16_t*>(q),

@@ -59,10 +59,12 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                           float scale, int p_mode, const int32_t* last_key,
                           void* ws, hipStream_t stream);
 
-// A prompt of n_rows rows in chunks of `chunk`: each chunk's cache write, then
-// its attention (as launch_cache_write + launch_prefill per chunk, with the
-// same bits); a split chunk's merge shares a launch with the next chunk's
-// cache write.  ws as launch_prefill's, sized for one chunk.
+// A prompt of n_rows rows in chunks of `chunk`, with the bits of
+// launch_cache_write + launch_prefill (no workspace) per chunk, in one
+// attention launch: a linear cache takes every row first; a ring's attended
+// keys go to a linear copy in ws (prefill_prompt_stage_bytes), and the
+// prompt's last rows enter the ring after the attention.
+size_t prefill_prompt_stage_bytes(int pos0, int n_rows, int Hkv, int D, int ring, int window);
 hipError_t launch_prefill_prompt(uint16_t* out, const uint16_t* q, const uint16_t* k,
                                  const uint16_t* v, uint16_t* kc, uint16_t* vc, int pos0,
                                  int n_rows, int chunk, int Hq, int Hkv, int D, int cap,
@@ -73,7 +75,8 @@ hipError_t launch_prefill_prompt(uint16_t* out, const uint16_t* q, const uint16_
 hipError_t launch_prefill_512(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                               const uint16_t* vc, int pos0, int n_rows, int Hq, int Hkv,
                               int cap, int ring, int window, float scale, int p_mode,
-                              const int32_t* last_key, hipStream_t stream);
+                              const int32_t* last_key, int base, int clamp_rows,
+                              hipStream_t stream);
 
 hipError_t launch_cache_write(uint16_t* kc, uint16_t* vc, const uint16_t* k,
                               const uint16_t* v, int pos0, int n_rows, int Hkv,

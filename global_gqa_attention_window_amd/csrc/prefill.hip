@@ -116,7 +116,8 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     int pos0, int n_rows, int Hq, int Hkv, int G, int HG, int cap,
                     int ring, int window, float c,
                     const int32_t* __restrict__ last_key, int S,
-                    float* __restrict__ part_acc, float* __restrict__ part_ml) {
+                    float* __restrict__ part_acc, float* __restrict__ part_ml, int pos_base,
+                    int clamp_rows) {
     constexpr int KB = PrefillCfg<D>::KB;
     constexpr int KPADP = 16;                // K padding per row (pair at 256)
     constexpr int VPADP = 16;                // V padding per row (pair at 256)
@@ -148,7 +149,8 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     // XCD-aware tile order: the hardware deals workgroup L to XCD L % 8, so
     // L is renumbered to put each XCD on a contiguous range of tiles ordered
     // KV group, head group, row tile: the workgroups sharing one L2 then
-    // stream the same K/V blocks at about the same time
+    // stream the same K/V blocks at about the same time.  Row tiles go last
+    // row first, so that in a long launch the longest walks start first
     // (SPLIT: the S workgroups of a tile are consecutive in that order)
     const int n_rt = (n_rows + 15) / 16;
     const int nwg = n_rt * Hkv * HG * (SPLIT ? S : 1);
@@ -156,7 +158,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int lam = (nwg % 8 == 0) ? (L % 8) * (nwg / 8) + L / 8 : L;
     const int sp = SPLIT ? lam % S : 0;              // range of the tile's blocks
     const int lt = SPLIT ? lam / S : lam;
-    const int rt = lt % n_rt;
+    const int rt = n_rt - 1 - lt % n_rt;        // later (longer) tiles first
     const int gh = lt / n_rt;                        // g * HG + head group
     const int r0 = rt * 16;
     const int g = gh / HG;
@@ -172,11 +174,15 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int t_row = pos0 + r0 + col;
     const int lo_row = window > 0 ? max(0, t_row - window + 1) : 0;
     // each row's last key: its own position, or last_key's value clamped to
-    // [own position, the chunk's last row]; the tile reads keys up to the
-    // largest of its rows' last keys (a wave-uniform value)
+    // [own position, the last row of the row's chunk of clamp_rows rows]; the
+    // tile reads keys up to the largest of its rows' last keys (a
+    // wave-uniform value)
     int t_hi = t_row;
-    if (last_key != nullptr && row_ok)
-        t_hi = min(max((int)last_key[r0 + col], t_row), pos0 + n_rows - 1);
+    if (last_key != nullptr && row_ok) {
+        const int r = r0 + col;
+        const int c_end = (int)min((long long)n_rows, (long long)(r - r % clamp_rows) + clamp_rows);
+        t_hi = min(max((int)last_key[r], t_row), pos0 + c_end - 1);
+    }
     int hi_m = row_ok ? t_hi : t_first;
     hi_m = max(hi_m, __shfl_xor(hi_m, 1));
     hi_m = max(hi_m, __shfl_xor(hi_m, 2));
@@ -229,7 +235,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     auto dma_plan = [&](const uint16_t* g, uint16_t* stage, int b, const uint16_t*& base,
                         uint32_t (&voff)[IPW], uint32_t& lds0) {
         const int p0 = b * KB;
-        const int s0 = ring ? p0 % cap : p0;
+        const int s0 = ring ? p0 % cap : p0 - pos_base;
         lds0 = lds_addr(stage);
         if (p0 >= lo_tile && p0 + KB - 1 <= hi_tile && s0 + KB <= cap) {
             base = g + (size_t)s0 * D;
@@ -240,7 +246,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
 #pragma unroll
             for (int i = 0; i < IPW; ++i) {
                 const int p = min(max(p0 + lane_row[i], lo_tile), hi_tile);
-                const int slot = ring ? p % cap : p;
+                const int slot = ring ? p % cap : p - pos_base;
                 voff[i] = (uint32_t)(slot * D + lane_col) * 2u;
             }
         }
@@ -301,8 +307,8 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     auto l2_prefetch = [&](int b) {
         if (wave >= 2) return;
         const int r = (rt * PF_ROWS) % KB + (lane * 8) / D;
-        const int p = min(b * KB + r, hi_tile);
-        const int slot = ring ? p % cap : p;
+        const int p = max(min(b * KB + r, hi_tile), lo_tile);
+        const int slot = ring ? p % cap : p - pos_base;
         const uint16_t* g = wave == 0 ? Kg : Vg;
         dma16_asm_sbase(g, (uint32_t)(slot * D + (lane * 8) % D) * 2u,
                         lds_addr(pf_lds[wave]));
@@ -753,6 +759,39 @@ void merge_write_kernel(uint16_t* __restrict__ out, const float* __restrict__ pa
                          (size_t)(b - n_merge_wg) * 256 + threadIdx.x);
 }
 
+// A prompt's keys and values as one linear span for a single launch: unit i
+// of Hkv * L * D / 8 copies eight bf16 of position base + l (l < L) of KV
+// head g into [g][l][D] of sk and sv, from the ring (slot p mod cap) below
+// pos0, from the prompt's k and v ([row][Hkv][D]) from pos0 on.
+__global__ __launch_bounds__(256)
+void stage_kernel(uint16_t* __restrict__ sk, uint16_t* __restrict__ sv,
+                  const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                  const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int pos0,
+                  int base, int L, int n_rows, int Hkv, int D, int cap) {
+    const int vpr = D / 8;
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (size_t)Hkv * L * vpr) return;
+    const int dv = (int)(i % vpr);
+    const size_t gl = i / vpr;
+    const int l = (int)(gl % L);
+    const int g = (int)(gl / L);
+    const int p = base + l;
+    size_t src;
+    const uint16_t *ks, *vs;
+    if (p < pos0) {
+        src = ((size_t)g * cap + (size_t)(p % cap)) * D;
+        ks = kc;
+        vs = vc;
+    } else {
+        src = ((size_t)(p - pos0) * Hkv + g) * D;
+        ks = k;
+        vs = v;
+    }
+    const size_t dst = gl * D + (size_t)dv * 8;
+    st16(sk + dst, ld16(ks + src + (size_t)dv * 8));
+    st16(sv + dst, ld16(vs + src + (size_t)dv * 8));
+}
+
 }  // namespace
 
 int prefill_key_block(int D, int p_mode) {
@@ -782,17 +821,19 @@ struct PrefillParts {
     float* ml = nullptr;
 };
 
-// The attention launch of one chunk; with S > 1 in parts, its merge is
-// still to come.
+// The attention launch over n_rows rows; with S > 1 in parts, its merge is
+// still to come.  base: the position of slot 0 of a linear cache (a staged
+// copy of a span of positions); clamp_rows: the chunk length whose last row
+// bounds each row's last key.
 hipError_t launch_prefill_attend(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                                  const uint16_t* vc, int pos0, int n_rows, int Hq, int Hkv,
                                  int D, int cap, int ring, int window, float scale,
-                                 int p_mode, const int32_t* last_key, void* ws,
-                                 hipStream_t stream, PrefillParts& parts) {
+                                 int p_mode, const int32_t* last_key, void* ws, int base,
+                                 int clamp_rows, hipStream_t stream, PrefillParts& parts) {
     parts = PrefillParts{};
     if (D == 512)
         return launch_prefill_512(out, q, kc, vc, pos0, n_rows, Hq, Hkv, cap, ring, window,
-                                  scale, p_mode, last_key, stream);
+                                  scale, p_mode, last_key, base, clamp_rows, stream);
     const int G = Hq / Hkv;
     const int HG = (G + 3) / 4;
     const float c = scale * ATTN_LOG2E;
@@ -803,7 +844,7 @@ hipError_t launch_prefill_attend(uint16_t* out, const uint16_t* q, const uint16_
 #define PF_LAUNCH(PP, SP)                                                                     \
     prefill_kernel<256, PP, SP><<<grid, 256, 0, stream>>>(                                    \
         out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key, S,      \
-        part_acc, part_ml)
+        part_acc, part_ml, base, clamp_rows)
     if (S > 1) {
         if (p_mode == ATTN_P_BF16X2) PF_LAUNCH(ATTN_P_BF16X2, true);
         else PF_LAUNCH(ATTN_P_BF16, true);
@@ -847,11 +888,18 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                           void* ws, hipStream_t stream) {
     PrefillParts parts;
     const hipError_t e = launch_prefill_attend(out, q, kc, vc, pos0, n_rows, Hq, Hkv, D, cap,
-                                               ring, window, scale, p_mode, last_key, ws,
-                                               stream, parts);
+                                               ring, window, scale, p_mode, last_key, ws, 0,
+                                               n_rows > 0 ? n_rows : 1, stream, parts);
     if (e != hipSuccess) return e;
     return launch_merge_write(out, n_rows, Hq, parts, nullptr, nullptr, nullptr, nullptr, 0, 0,
                               Hkv, D, cap, ring, stream);
+}
+
+size_t prefill_prompt_stage_bytes(int pos0, int n_rows, int Hkv, int D, int ring, int window) {
+    if (!ring) return 0;
+    const long long base = std::max(0, pos0 - window + 1);
+    const long long L = (long long)pos0 + n_rows - base;
+    return (size_t)2 * Hkv * L * D * sizeof(uint16_t);
 }
 
 hipError_t launch_prefill_prompt(uint16_t* out, const uint16_t* q, const uint16_t* k,
@@ -859,21 +907,35 @@ hipError_t launch_prefill_prompt(uint16_t* out, const uint16_t* q, const uint16_
                                  int n_rows, int chunk, int Hq, int Hkv, int D, int cap,
                                  int ring, int window, float scale, int p_mode,
                                  const int32_t* last_key, void* ws, hipStream_t stream) {
-    hipError_t e = launch_cache_write(kc, vc, k, v, pos0, std::min(chunk, n_rows), Hkv, D, cap,
-                                      ring, stream);
-    for (int r0 = 0; e == hipSuccess && r0 < n_rows; r0 += chunk) {
-        const int m = std::min(chunk, n_rows - r0);
-        const int r1 = r0 + m;
-        const int m_next = std::min(chunk, n_rows - r1);
-        const size_t qo = (size_t)r0 * Hq * D;
-        PrefillParts parts;
-        e = launch_prefill_attend(out + qo, q + qo, kc, vc, pos0 + r0, m, Hq, Hkv, D, cap, ring,
-                                  window, scale, p_mode, last_key ? last_key + r0 : nullptr, ws,
-                                  stream, parts);
-        if (e != hipSuccess) break;
-        const size_t ko = (size_t)r1 * Hkv * D;
-        e = launch_merge_write(out + qo, m, Hq, parts, kc, vc, k + ko, v + ko, pos0 + r1,
-                               m_next, Hkv, D, cap, ring, stream);
+    PrefillParts parts;                          // (one launch, no split)
+    if (!ring) {
+        // every row into the cache first: no chunk reads a slot another
+        // chunk writes, so one launch attends the whole prompt
+        hipError_t e = launch_cache_write(kc, vc, k, v, pos0, n_rows, Hkv, D, cap, ring, stream);
+        if (e != hipSuccess) return e;
+        return launch_prefill_attend(out, q, kc, vc, pos0, n_rows, Hq, Hkv, D, cap, 0, window,
+                                     scale, p_mode, last_key, nullptr, 0, chunk, stream, parts);
     }
-    return e;
+    // A ring: chunk c + 1's rows would overwrite keys chunk c still reads, so
+    // every key the prompt attends (the window before pos0 from the ring, the
+    // prompt's own from k and v) goes to a linear copy in the workspace, one
+    // launch attends the whole prompt over it, and the prompt's last rows
+    // then enter the ring (those the chunked path leaves there).
+    const int base = std::max(0, pos0 - window + 1);
+    const int L = pos0 + n_rows - base;
+    uint16_t* sk = static_cast<uint16_t*>(ws);
+    uint16_t* sv = sk + (size_t)Hkv * L * D;
+    const size_t units = (size_t)Hkv * L * (D / 8);
+    stage_kernel<<<(unsigned)((units + 255) / 256), 256, 0, stream>>>(sk, sv, kc, vc, k, v, pos0,
+                                                                      base, L, n_rows, Hkv, D,
+                                                                      cap);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_prefill_attend(out, q, sk, sv, pos0, n_rows, Hq, Hkv, D, L, 0, window, scale,
+                              p_mode, last_key, nullptr, base, chunk, stream, parts);
+    if (e != hipSuccess) return e;
+    const int tail = std::min(n_rows, cap);
+    const size_t ko = (size_t)(n_rows - tail) * Hkv * D;
+    return launch_cache_write(kc, vc, k + ko, v + ko, pos0 + n_rows - tail, tail, Hkv, D, cap,
+                              ring, stream);
 }

@@ -41,7 +41,7 @@ void prefill_roles_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict
                           const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                           int pos0, int n_rows, int Hq, int Hkv, int G, int HG, int cap,
                           int ring, int window, float c,
-                          const int32_t* __restrict__ last_key) {
+                          const int32_t* __restrict__ last_key, int pos_base, int clamp_rows) {
     constexpr int D = P5_D, KB = P5_KB, HD = P5_H;
     constexpr bool X2 = PM == ATTN_P_BF16X2;
     constexpr int KT = KB / 16;              // 16-key score tiles per block
@@ -73,12 +73,14 @@ void prefill_roles_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict
 
     // XCD-aware tile order (workgroup L runs on XCD L % 8): each XCD takes a
     // contiguous range of (KV group, head group, row tile), so the
-    // workgroups sharing an L2 stream the same K/V blocks together
+    // workgroups sharing an L2 stream the same K/V blocks together; row tiles
+    // go last row first, so that in a long launch the longest walks start
+    // first
     const int n_rt = (n_rows + 15) / 16;
     const int nwg = n_rt * Hkv * HG;
     const int L = blockIdx.x;
     const int lam = (nwg % 8 == 0) ? (L % 8) * (nwg / 8) + L / 8 : L;
-    const int rt = lam % n_rt;
+    const int rt = n_rt - 1 - lam % n_rt;       // later (longer) tiles first
     const int gh = lam / n_rt;
     const int r0 = rt * 16;
     const int g = gh / HG;
@@ -92,11 +94,15 @@ void prefill_roles_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict
     const int t_row = pos0 + r0 + col;
     const int lo_row = window > 0 ? max(0, t_row - window + 1) : 0;
     // each row's last key: its own position, or last_key's value clamped to
-    // [own position, the chunk's last row]; the tile reads keys up to the
-    // largest of its rows' last keys (a wave-uniform value)
+    // [own position, the last row of the row's chunk of clamp_rows rows]; the
+    // tile reads keys up to the largest of its rows' last keys (a
+    // wave-uniform value)
     int t_hi = t_row;
-    if (last_key != nullptr && row_ok)
-        t_hi = min(max((int)last_key[r0 + col], t_row), pos0 + n_rows - 1);
+    if (last_key != nullptr && row_ok) {
+        const int r = r0 + col;
+        const int c_end = (int)min((long long)n_rows, (long long)(r - r % clamp_rows) + clamp_rows);
+        t_hi = min(max((int)last_key[r], t_row), pos0 + c_end - 1);
+    }
     int hi_m = row_ok ? t_hi : t_first;
     hi_m = max(hi_m, __shfl_xor(hi_m, 1));
     hi_m = max(hi_m, __shfl_xor(hi_m, 2));
@@ -130,7 +136,7 @@ void prefill_roles_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict
     auto dma_plan = [&](const uint16_t* gsrc, uint16_t* stage, int b, const uint16_t*& base,
                         uint32_t (&voff)[IPW], uint32_t& lds0) {
         const int p0 = b * KB;
-        const int s0 = ring ? p0 % cap : p0;
+        const int s0 = ring ? p0 % cap : p0 - pos_base;
         lds0 = lds_addr(stage);
         if (p0 >= lo_tile && p0 + KB - 1 <= hi_tile && s0 + KB <= cap) {
             base = gsrc + (size_t)s0 * D;
@@ -141,7 +147,7 @@ void prefill_roles_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict
 #pragma unroll
             for (int i = 0; i < IPW; ++i) {
                 const int p = min(max(p0 + lane_row[i], lo_tile), hi_tile);
-                const int slot = ring ? p % cap : p;
+                const int slot = ring ? p % cap : p - pos_base;
                 voff[i] = (uint32_t)(slot * D + lane * 8) * 2u;
             }
         }
@@ -375,16 +381,19 @@ void prefill_roles_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict
 hipError_t launch_prefill_512(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                               const uint16_t* vc, int pos0, int n_rows, int Hq, int Hkv,
                               int cap, int ring, int window, float scale, int p_mode,
-                              const int32_t* last_key, hipStream_t stream) {
+                              const int32_t* last_key, int base, int clamp_rows,
+                              hipStream_t stream) {
     const int G = Hq / Hkv;
     const int HG = (G + 3) / 4;
     const float c = scale * ATTN_LOG2E;
     dim3 grid(((n_rows + 15) / 16) * Hkv * HG);
     if (p_mode == ATTN_P_BF16X2)
         prefill_roles_kernel<ATTN_P_BF16X2><<<grid, 512, 0, stream>>>(
-            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key);
+            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key, base,
+            clamp_rows);
     else
         prefill_roles_kernel<ATTN_P_BF16><<<grid, 512, 0, stream>>>(
-            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key);
+            out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key, base,
+            clamp_rows);
     return hipGetLastError();
 }

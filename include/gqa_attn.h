@@ -383,29 +383,39 @@ int attn_cache_write(void* k_cache, void* v_cache, const void* k,
                      int head_dim, int cache_cap, int ring, void* stream);
 
 /*
- * A whole prompt through one layer, chunk after chunk (PR #975 commits: the
- * prompt is fed in chunks, and a chunk's keys and values enter the cache
- * before its attention reads them): rows r0 .. r0 + m - 1 of each chunk of
- * `chunk` rows (the last may be shorter) are written into the cache, then
- * attended as attn_prefill_ws attends them.  The outputs and the cache are
- * bit for bit those of attn_cache_write + attn_prefill_ws per chunk; the
- * library drives the sequence, and a split chunk's merge shares a launch
- * with the next chunk's cache write.
+ * A whole prompt through one layer, in chunks (PR #975 commits: the prompt is
+ * fed in chunks, and a chunk's keys and values enter the cache before its
+ * attention reads them): rows r0 .. r0 + m - 1 of each chunk of `chunk` rows
+ * (the last may be shorter) are attended as attn_prefill attends them after
+ * attn_cache_write has put them in the cache.  The outputs and the final
+ * cache are bit for bit those of attn_cache_write + attn_prefill chunk by
+ * chunk.  Key blocks sit on absolute positions, so a row's bits do not depend
+ * on the chunks, and the library attends the whole prompt in one launch:
+ * into a linear cache every row is written first; with a ring, where chunk c
+ * + 1 would overwrite keys chunk c still reads, the keys the prompt attends
+ * (the window before pos0 from the ring, the prompt's own from k and v) go
+ * to a linear copy in the workspace, and the prompt's last rows enter the
+ * ring after the attention.
  *
  *   out, q            device bf16 [n_rows][Hq][D]
  *   k, v              device bf16 [n_rows][Hkv][D], the prompt's keys and
  *                     values (rotated, normed), row r at position pos0 + r
- *   k_cache, v_cache  device bf16 [Hkv][cap][D], written and read
+ *   k_cache, v_cache  device bf16 [Hkv][cap][D], written (and read)
  *   chunk             rows per chunk, >= 1 (else ATTN_E_RANGE); every chunk
  *                     must meet attn_prefill's conditions (a ring: cap >= W +
  *                     min(chunk, n_rows) - 1; a linear cache: pos0 + n_rows
  *                     <= cap, else ATTN_E_CACHE)
- *   last_key          NULL, or device int32 [n_rows]: chunk by chunk as
- *                     attn_prefill takes it (values clamped to the chunk)
- *   workspace        NULL (no split), or as attn_prefill_ws's for
- *                     min(chunk, n_rows) rows
+ *   last_key          NULL, or device int32 [n_rows]: as attn_prefill takes
+ *                     it chunk by chunk (each value clamped to the last row of
+ *                     its row's chunk)
+ *   workspace         ring: device, 16-byte aligned, >=
+ *                     attn_prefill_prompt_workspace_bytes(...) bytes (else
+ *                     ATTN_E_WORKSPACE), contents ignored; a linear cache
+ *                     needs none (NULL)
  *   (the rest as attn_prefill)
  */
+size_t attn_prefill_prompt_workspace_bytes(int pos0, int n_rows, int n_kv_heads, int head_dim,
+                                           int ring, int window);
 int attn_prefill_prompt(void* out, const void* q, const void* k, const void* v,
                         void* k_cache, void* v_cache, int pos0, int n_rows, int chunk,
                         int n_q_heads, int n_kv_heads, int head_dim, int cache_cap, int ring,

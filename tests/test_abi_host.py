@@ -237,8 +237,20 @@ def _prompt(ga, ws=P, ws_bytes=1 << 30, **kw):
                                        a["last"], ws, ws_bytes, None)
 
 
+def test_prefill_prompt_workspace_bytes(ga):
+    # a ring's attended span (the window before pos0 and the prompt) as K and
+    # V copies [Hkv][span][D]; a linear cache needs none
+    f = ga.attn_prefill_prompt_workspace_bytes
+    assert f(0, 8192, 4, 256, 1, 1024) == 2 * 4 * 8192 * 256 * 2
+    assert f(5000, 8192, 4, 256, 1, 1024) == 2 * 4 * (1023 + 8192) * 256 * 2
+    assert f(100, 50, 2, 512, 1, 1024) == 2 * 2 * 150 * 512 * 2
+    assert f(0, 32768, 2, 512, 0, 0) == 0
+    assert f(0, 10, 2, 384, 1, 8) == 0 and f(0, 10, 2, 256, 1, 0) == 0
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(chunk=0), "ATTN_E_RANGE"), (dict(n=-1), "ATTN_E_RANGE"),
+    (dict(ws=None, ws_bytes=0), "ATTN_E_WORKSPACE"),   # a ring needs the span's copy
     (dict(chunk=130), "ATTN_E_CACHE"),                 # ring: cap < W + chunk - 1
     (dict(ring=0, window=0, cap=8000), "ATTN_E_CACHE"),  # linear: the prompt passes cap
     (dict(ws_bytes=100), "ATTN_E_WORKSPACE"), (dict(ws=P + 8), "ATTN_E_ALIGN"),
@@ -255,6 +267,14 @@ def test_prefill_prompt_refusals(ga, kw, status):
 @no_gpu
 def test_prefill_prompt_zero_rows_is_a_no_op(ga):
     assert _prompt(ga, n=0, out=None, k=None, ws=None, ws_bytes=0) == 0
+
+
+@no_gpu
+def test_prefill_prompt_linear_needs_no_workspace(ga):
+    # a linear cache passes every check without a workspace (the first
+    # refusal left is the NULL output)
+    assert _prompt(ga, ring=0, window=0, cap=8192, ws=None, ws_bytes=0,
+                   out=None) == _status("ATTN_E_NULL")
 
 
 @pytest.mark.parametrize("kw,status", [
