@@ -740,23 +740,11 @@ ATTN_DEV void prefill_merge_unit(uint16_t* __restrict__ out, const float* __rest
     *reinterpret_cast<u32x2*>(out + rh * D + d) = u32x2{pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
 }
 
-// The merge of a split launch's range partials (workgroups below n_merge_wg),
-// and with it, in a chunked prompt, the cache write of the next chunk (the
-// rest): two independent steps in one launch.  Chunk c's attention has finished, so the ring
-// slots the write takes are no longer read, and the merge reads no cache.
 template <int D>
 __global__ __launch_bounds__(256)
-void merge_write_kernel(uint16_t* __restrict__ out, const float* __restrict__ part_acc,
-                        const float* __restrict__ part_ml, int n_rh, int S, int n_merge_wg,
-                        uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
-                        const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-                        int pos0, int n_rows, int Hkv, int cap, int ring) {
-    const int b = blockIdx.x;
-    if (b < n_merge_wg)
-        prefill_merge_unit<D>(out, part_acc, part_ml, n_rh, S, (long long)b * 256 + threadIdx.x);
-    else
-        cache_write_unit(kc, vc, k, v, pos0, n_rows, Hkv, D, cap, ring,
-                         (size_t)(b - n_merge_wg) * 256 + threadIdx.x);
+void prefill_merge_kernel(uint16_t* __restrict__ out, const float* __restrict__ part_acc,
+                          const float* __restrict__ part_ml, int n_rh, int S) {
+    prefill_merge_unit<D>(out, part_acc, part_ml, n_rh, S, (long long)blockIdx.x * 256 + threadIdx.x);
 }
 
 // A prompt's keys and values as one linear span for a single launch: unit i
@@ -859,23 +847,14 @@ hipError_t launch_prefill_attend(uint16_t* out, const uint16_t* q, const uint16_
     return hipGetLastError();
 }
 
-// The merge of a split chunk (rows of out) and the cache write of the next
-// chunk's n_next rows, in one launch where both are due; either alone
-// otherwise, or nothing.
-hipError_t launch_merge_write(uint16_t* out, int n_rows, int Hq, const PrefillParts& parts,
-                              uint16_t* kc, uint16_t* vc, const uint16_t* k,
-                              const uint16_t* v, int pos_next, int n_next, int Hkv, int D,
-                              int cap, int ring, hipStream_t stream) {
+// The merge of a split launch's range partials into the rows of out
+// (nothing when the launch did not split; splits happen at head dim 256).
+hipError_t launch_prefill_merge(uint16_t* out, int n_rows, int Hq, const PrefillParts& parts,
+                                hipStream_t stream) {
+    if (parts.S <= 1) return hipSuccess;
     const long long n_rh = (long long)n_rows * Hq;
-    const unsigned merge_wg = parts.S > 1 ? (unsigned)((n_rh * (256 / 4) + 255) / 256) : 0u;
-    const unsigned write_wg = (unsigned)(((size_t)n_next * Hkv * (D / 8) + 255) / 256);
-    if (merge_wg == 0 && write_wg == 0) return hipSuccess;
-    if (merge_wg == 0)
-        return launch_cache_write(kc, vc, k, v, pos_next, n_next, Hkv, D, cap, ring, stream);
-    // (splits happen at head dim 256 only)
-    merge_write_kernel<256><<<merge_wg + write_wg, 256, 0, stream>>>(
-        out, parts.acc, parts.ml, (int)n_rh, parts.S, (int)merge_wg, kc, vc, k, v, pos_next,
-        n_next, Hkv, cap, ring);
+    prefill_merge_kernel<256><<<(unsigned)((n_rh * (256 / 4) + 255) / 256), 256, 0, stream>>>(
+        out, parts.acc, parts.ml, (int)n_rh, parts.S);
     return hipGetLastError();
 }
 
@@ -891,8 +870,7 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, const uint16_t* kc,
                                                ring, window, scale, p_mode, last_key, ws, 0,
                                                n_rows > 0 ? n_rows : 1, stream, parts);
     if (e != hipSuccess) return e;
-    return launch_merge_write(out, n_rows, Hq, parts, nullptr, nullptr, nullptr, nullptr, 0, 0,
-                              Hkv, D, cap, ring, stream);
+    return launch_prefill_merge(out, n_rows, Hq, parts, stream);
 }
 
 size_t prefill_prompt_stage_bytes(int pos0, int n_rows, int Hkv, int D, int ring, int window) {
