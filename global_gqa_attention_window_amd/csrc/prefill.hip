@@ -9,9 +9,10 @@
 // over 128-dim slices (the score accumulates 32-wide steps in ascending d, so
 // 128-wide slices add in slice order) and P may be kept as two bf16 halves.
 //
-// MI355X design.  A workgroup of four waves takes one 16-row tile of the
-// chunk and four query heads of one KV group; wave w owns head w: 16 rows x
-// the whole head dim, so its softmax state never leaves the wave.  The four
+// MI355X design.  A workgroup of NW waves (four, or eight in launches with
+// enough tiles to fill the chip twice over) takes one 16-row tile of the
+// chunk and NW query heads of one KV group; wave w owns head w: 16 rows x
+// the whole head dim, so its softmax state never leaves the wave.  The
 // heads share every key block: K and V rows land in LDS by direct
 // global->LDS loads (1 KiB of whole rows per instruction, no registers, no
 // VALU), two stages, the next block in flight while the current one is
@@ -27,7 +28,9 @@
 //                             hi and lo halves, two products) as B; the V^T
 //                             operand comes straight from the row-major V
 //                             block through two transpose reads.
-// One wave runs per SIMD, so the wave itself must keep its matrix unit fed:
+// One wave runs per SIMD (two at NW = 8, which hide one wave's LDS reads and
+// softmax behind the other's products), so the wave itself must keep its
+// matrix unit fed:
 // an iteration issues the scores of block b + 1 (K operands eight products
 // ahead, with the accumulator rescale that block b needs in the VALU slots
 // beside them), then block b's P.V with block b + 1's mask and softmax cut
@@ -109,8 +112,8 @@ ATTN_DEV int split_start(int n, int S, int s) {
     return (int)((2 * n * num + den) / (2 * den));
 }
 
-template <int D, int PM, bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int PM, bool SPLIT, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
                     int pos0, int n_rows, int Hq, int Hkv, int G, int HG, int cap,
@@ -129,8 +132,8 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     constexpr int DT = D / 16;               // 16-wide d tiles of the output
     constexpr int LPR = D / 8;               // lanes that move one row
     constexpr int INSTR = KB * LPR / 64;     // DMA instructions per K (or V) block
-    constexpr int IPW = INSTR / 4;           // ... per wave
-    static_assert(IPW * 4 == INSTR, "DMA split");
+    constexpr int IPW = INSTR / NW;          // ... per wave
+    static_assert(IPW * NW == INSTR, "DMA split");
     constexpr int K16 = row_pos<D, KPADP>(16);     // offset of the next 16 rows
     constexpr int V16 = row_pos<D, VPADP>(16);
 
@@ -162,7 +165,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int gh = lt / n_rt;                        // g * HG + head group
     const int r0 = rt * 16;
     const int g = gh / HG;
-    const int hl = (gh % HG) * 4 + wave;
+    const int hl = (gh % HG) * NW + wave;
     const bool head_ok = hl < G;
     const int h = g * G + (head_ok ? hl : 0);
     const int nvalid = min(16, n_rows - r0);
@@ -823,22 +826,30 @@ hipError_t launch_prefill_attend(uint16_t* out, const uint16_t* q, const uint16_
         return launch_prefill_512(out, q, kc, vc, pos0, n_rows, Hq, Hkv, cap, ring, window,
                                   scale, p_mode, last_key, base, clamp_rows, stream);
     const int G = Hq / Hkv;
-    const int HG = (G + 3) / 4;
     const float c = scale * ATTN_LOG2E;
     const int S = ws ? prefill_split_count(n_rows, Hq, Hkv, D) : 1;
-    dim3 grid(((n_rows + 15) / 16) * Hkv * HG * S);
+    const int n_rt = (n_rows + 15) / 16;
+    // eight waves (heads) a workgroup when a group has more than four heads
+    // and the launch still fills every CU with such workgroups (a wave's
+    // arithmetic does not depend on the workgroup's width)
+    const bool wide = S == 1 && G > 4 && (long long)n_rt * Hkv * ((G + 7) / 8) >= 256;
+    const int HG = wide ? (G + 7) / 8 : (G + 3) / 4;
+    dim3 grid(n_rt * Hkv * HG * S);
     float* part_acc = static_cast<float*>(ws);
     float* part_ml = S > 1 ? part_acc + (size_t)n_rows * Hq * S * D : nullptr;
-#define PF_LAUNCH(PP, SP)                                                                     \
-    prefill_kernel<256, PP, SP><<<grid, 256, 0, stream>>>(                                    \
+#define PF_LAUNCH(PP, SP, NN)                                                                 \
+    prefill_kernel<256, PP, SP, NN><<<grid, 64 * NN, 0, stream>>>(                            \
         out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key, S,      \
         part_acc, part_ml, base, clamp_rows)
     if (S > 1) {
-        if (p_mode == ATTN_P_BF16X2) PF_LAUNCH(ATTN_P_BF16X2, true);
-        else PF_LAUNCH(ATTN_P_BF16, true);
+        if (p_mode == ATTN_P_BF16X2) PF_LAUNCH(ATTN_P_BF16X2, true, 4);
+        else PF_LAUNCH(ATTN_P_BF16, true, 4);
+    } else if (wide) {
+        if (p_mode == ATTN_P_BF16X2) PF_LAUNCH(ATTN_P_BF16X2, false, 8);
+        else PF_LAUNCH(ATTN_P_BF16, false, 8);
     } else {
-        if (p_mode == ATTN_P_BF16X2) PF_LAUNCH(ATTN_P_BF16X2, false);
-        else PF_LAUNCH(ATTN_P_BF16, false);
+        if (p_mode == ATTN_P_BF16X2) PF_LAUNCH(ATTN_P_BF16X2, false, 4);
+        else PF_LAUNCH(ATTN_P_BF16, false, 4);
     }
 #undef PF_LAUNCH
     parts.S = S;

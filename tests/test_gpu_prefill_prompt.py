@@ -1,7 +1,8 @@
 """GPU checks of attn_prefill_prompt, the whole-prompt entry point: its
 outputs and final caches equal attn_cache_write + attn_prefill chunk by chunk
 bit for bit (one attention launch over the whole prompt: key blocks sit on
-absolute positions; a ring's attended span goes to a linear copy first), on
+absolute positions; a ring's attended span goes to a linear copy first; large
+launches take eight heads a workgroup, with the same per-head arithmetic), on
 the 8k sliding prompt and on small shapes with ragged chunks, rings that wrap,
 positions past the cache start, per-row last keys clamped per chunk, NaN in
 unwritten slots and both head dims; two shapes are also checked against the
@@ -69,6 +70,7 @@ def test_prompt_sliding_8k_equals_chunk_calls(ga):
     (512, 8, 2, 1, 300, 200, 50, 260, 77, P_BF16X2),        # head dim 512 ring, pos0 > 0
     (256, 6, 2, 0, 200, 5, 16, 100, 0, P_BF16),             # G = 3, tiny window
     (256, 8, 1, 0, 64, 0, 1000, 60, 0, P_BF16),             # one chunk shorter than chunk
+    (256, 12, 2, 1, 1100, 1000, 100, 2048, 0, P_BF16X2),    # G = 6 on eight-wave workgroups
 ])
 def test_prompt_shapes_equal_chunk_calls(ga, D, Hq, Hkv, ring, cap, window, chunk, n, pos0,
                                          p_mode):
