@@ -71,6 +71,7 @@ def test_prompt_sliding_8k_equals_chunk_calls(ga):
     (256, 6, 2, 0, 200, 5, 16, 100, 0, P_BF16),             # G = 3, tiny window
     (256, 8, 1, 0, 64, 0, 1000, 60, 0, P_BF16),             # one chunk shorter than chunk
     (256, 12, 2, 1, 1100, 1000, 100, 2048, 0, P_BF16X2),    # G = 6 on eight-wave workgroups
+    (256, 2, 2, 1, 64, 1, 16, 130, 5, P_BF16X2),            # window of 1, pos0 > 0
 ])
 def test_prompt_shapes_equal_chunk_calls(ga, D, Hq, Hkv, ring, cap, window, chunk, n, pos0,
                                          p_mode):
@@ -138,4 +139,20 @@ def test_prompt_nan_in_unwritten_slots(ga):
     assert not np.any(((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0))
     want, _ = run_prefill(ga, q, k, v, Hkv, cap, 1, W, 1 / 16, P_BF16, chunk,
                           caches=(kc.clone(), vc.clone()))
+    assert np.array_equal(got, want)
+
+
+def test_prompt_last_key_eight_wave_launch(ga):
+    """Per-row last keys (image spans, some crossing chunk ends) in a launch
+    large enough for eight-wave workgroups: the chunked path's bits."""
+    D, Hq, Hkv, cap, W, chunk, n = 256, 32, 4, 1152, 1024, 128, 2048
+    rng = np.random.default_rng(12)
+    q = randn_bf16_bits(rng, (n, Hq, D))
+    k = randn_bf16_bits(rng, (n, Hkv, D))
+    v = randn_bf16_bits(rng, (n, Hkv, D))
+    last = np.arange(n, dtype=np.int64)
+    for a, b in ((100, 180), (250, 270), (700, 900), (1500, 1536), (2000, 2047)):
+        last[a:b] = b - 1
+    got, _, _ = _prompt(ga, q, k, v, Hkv, cap, 1, W, 1 / 16, P_BF16, chunk, last_key=last)
+    want, _ = run_prefill(ga, q, k, v, Hkv, cap, 1, W, 1 / 16, P_BF16, chunk, last_key=last)
     assert np.array_equal(got, want)
