@@ -345,9 +345,11 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     };
 
     constexpr int NS = KT * QST;                 // score products per block
-    constexpr int KPF = 8;                       // K operand reads in flight
+    // K operand reads in flight (at two waves a SIMD the other wave covers
+    // the read latency, and shallower prefetch keeps registers in VGPRs)
+    constexpr int KPF = NW == 8 ? 2 : 8;
     constexpr int NPV = KS * DT;                 // V^T operands per block
-    constexpr int VPF = 4;                       // V^T operands in flight
+    constexpr int VPF = KPF / 2;                 // V^T operands in flight
     constexpr int NE = 8 * KS;                   // probabilities per lane per block
     static_assert(KPF == 2 * VPF, "the V^T reads fill the last KPF score steps");
     static_assert(IPW * DMA_EVERY <= NS && IPW * DMA_EVERY <= NPV, "DMA issues fit the steps");
