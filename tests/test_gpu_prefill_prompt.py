@@ -68,6 +68,7 @@ def test_prompt_sliding_8k_equals_chunk_calls(ga):
     (512, 32, 2, 0, 1500, 0, 512, 1100, 0, P_BF16X2),       # head dim 512
     (512, 16, 1, 1, 96, 33, 64, 200, 0, P_BF16),            # ring < block span
     (512, 8, 2, 1, 300, 200, 50, 260, 77, P_BF16X2),        # head dim 512 ring, pos0 > 0
+    (512, 8, 2, 1, 300, 200, 50, 260, 500, P_BF16X2),       # ... staged span not from slot 0
     (256, 6, 2, 0, 200, 5, 16, 100, 0, P_BF16),             # G = 3, tiny window
     (256, 8, 1, 0, 64, 0, 1000, 60, 0, P_BF16),             # one chunk shorter than chunk
     (256, 12, 2, 1, 1100, 1000, 100, 2048, 0, P_BF16X2),    # G = 6 on eight-wave workgroups
