@@ -51,7 +51,7 @@ void prefill_roles_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict
     constexpr int BLK = KB * ROW;
     constexpr int IPW = KB / 4;              // DMA instructions (1 KiB rows) per wave per block
     constexpr int NS = KT * QS;              // K operands per block
-    constexpr int KPF = 8;                   // K operand reads in flight
+    constexpr int KPF = 4;                   // K operand reads in flight
     constexpr int VPF = 4;                   // V^T operands read ahead
     constexpr int DMA_K_EVERY = NS / IPW;
     constexpr int DMA_V_EVERY = DTH / IPW;
