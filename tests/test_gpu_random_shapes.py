@@ -5,12 +5,14 @@ heads, a GQA group of 1-16 query heads (including sizes no fixed test uses,
 such as 5, 6 and 12), a linear or ring cache, a window or none, positions
 before, inside and past the cache, decode windows of 1-16 rows, prompt
 chunks of 1-519 rows and either P mode.  Every output element is checked
-with the oracle's range test, as in the fixed-shape tests.
+with the oracle's range test, as in the fixed-shape tests; each prompt also
+goes through attn_prefill_prompt (one launch), which must give the chunked
+path's outputs and final caches bit for bit.
 """
 import numpy as np
 import pytest
 
-from gpu_util import DEV, run_decode, run_decode_rows, run_prefill, say, up
+from gpu_util import DEV, down, run_decode, run_decode_rows, run_prefill, say, up
 from oracle import attn_ref
 from oracle.contract import key_block
 from synthetic.gen import randn_bf16_bits
@@ -86,8 +88,23 @@ def test_random_shape(ga, case):
                 b = min(pos0, a + step)
                 ga.attn_cache_write(kc, vc, up(k[a:b]), up(v[a:b]), a, b - a, Hkv, D, cap, ring)
             caches = (kc, vc)
-        got, _ = run_prefill(ga, q, k, v, Hkv, cap, ring, W, c["scale"], c["p_mode"], c["chunk"],
-                             pos0=pos0, caches=caches)
+        before = None if caches is None else tuple(t.clone() for t in caches)
+        got, (kc1, vc1) = run_prefill(ga, q, k, v, Hkv, cap, ring, W, c["scale"], c["p_mode"],
+                                      c["chunk"], pos0=pos0, caches=caches)
+        # the whole prompt in one launch: the same bits and the same caches
+        if before is None:
+            kc2 = torch.zeros((Hkv, cap, D), dtype=torch.int16, device=DEV)
+            vc2 = torch.zeros_like(kc2)
+        else:
+            kc2, vc2 = before
+        out2 = torch.empty((n, Hq, D), dtype=torch.int16, device=DEV)
+        nb = ga.attn_prefill_prompt_workspace_bytes(pos0, n, Hkv, D, ring, W)
+        ws = torch.empty(nb, dtype=torch.uint8, device=DEV) if ring else None
+        ga.attn_prefill_prompt(out2, up(q), up(k[pos0:]), up(v[pos0:]), kc2, vc2, pos0, n,
+                               c["chunk"], Hq, Hkv, D, cap, ring, W, c["scale"], c["p_mode"],
+                               workspace=ws)
+        assert np.array_equal(down(out2), got), (case, c)
+        assert np.array_equal(down(kc2), down(kc1)) and np.array_equal(down(vc2), down(vc1))
         ref = attn_ref.prefill(q, k, v, pos0, Hkv, W, c["scale"], c["p_mode"],
                                key_block(D, c["p_mode"]))
     else:
