@@ -170,8 +170,9 @@ void prefill_roles_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict
         const int hl = hg0 + rw;
         const bool okh = hl < G;
         const int h = g * G + (okh ? hl : 0);
-        // Q^T operands over the whole head, in AGPRs: Q[row col][h][32 st +
-        // 8 grp .. +7]
+        // Q^T operands over the whole head, held in registers for the whole
+        // pass: Q[row col][h][32 st + 8 grp .. +7]. Left to the allocator
+        // (no AGPR pin), they take VGPRs with no spill at two waves per SIMD.
         u32x4 qreg[QS];
         {
             const uint16_t* qrow = q + ((size_t)(r0 + (row_ok ? col : 0)) * Hq + h) * D + 8 * grp;
@@ -180,8 +181,6 @@ void prefill_roles_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict
                 const u32x4 z = {0u, 0u, 0u, 0u};
                 qreg[st] = (okh && row_ok) ? ld16(qrow + 32 * st) : z;
             }
-#pragma unroll
-            for (int st = 0; st < QS; ++st) asm volatile("" : "+a"(qreg[st]));
         }
         const int kofs = col * ROW + 8 * grp;
         // K operand j: tile j & 1, dims 32 (j >> 1) + 8 grp .. +7
