@@ -30,10 +30,12 @@ constexpr int CHUNK = ATTN_DECODE_CHUNK;
 // A matrix-core column is one (row, query head) pair: a 16-column tile holds
 // RPT = 16 / G rows of the G query heads of a KV head.  32-key blocks of K
 // and V are staged in LDS by direct global->LDS loads shared by a
-// workgroup's four waves.  At head dim 512 a workgroup takes 4 / DS column
-// tiles of one (stream, KV head, run of chunks); the DS waves of a tile split
-// its output d range (all of them form the tile's scores, so a column's
-// arithmetic is the same for every DS); two block stages.  At head dim 256 a
+// workgroup's waves.  At head dim 512 a workgroup takes 4 / DS column tiles
+// of one (stream, KV head, run of chunks); the DS waves of a tile split its
+// output d range (all of them form the tile's scores, so a column's
+// arithmetic is the same for every DS); two block stages.  Four tiles go to
+// decode_roles_kernel, which splits each tile's work between a scorer wave
+// and a P.V wave with the same per-column arithmetic.  At head dim 256 a
 // workgroup takes one tile: the run's even blocks go to waves 0 and 1 and its
 // odd blocks to waves 2 and 3, each pair splitting d in two, so a block's K
 // rows are read and its scores formed by two waves instead of four; each
@@ -765,6 +767,338 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     }
 }
 
+// Decode windows at head dim 512 over four column tiles a workgroup (the
+// shapes that give one tile to each of four waves above), in two roles on
+// eight waves, two per SIMD, as the head-dim-512 prompt kernel splits its
+// work: scorer w (waves 0-3) forms tile w's scores, reference maximum and
+// probability pieces and hands the pieces and the rescale factor over
+// through LDS; P.V wave w (waves 4-7) holds tile w's accumulator over all
+// 512 dims and adds V^T . {hi, mid, lo} to it.  With one wave a SIMD a
+// wave's K reads and softmax cannot hide behind its own products; here the
+// scorer of block b + 1 and the P.V wave of block b share each SIMD.  A step
+// is one barrier: scorers take block i + 1 (K(i + 1) in stage (i + 1) - lo,
+// loading K(i + 2)) while the P.V waves take block i (V(i), loading
+// V(i + 1)).  Every column's arithmetic is the four-wave kernel's, step for
+// step (the same score chains, the same lazy maximum, the same pieces, the
+// same product order per accumulator), so the bits are those of every other
+// form and do not depend on the window width.
+template <bool NTL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_roles_kernel(const uint16_t* __restrict__ q,
+                         const uint16_t* __restrict__ kc,
+                         const uint16_t* __restrict__ vc,
+                         const int32_t* __restrict__ pos,
+                         float* __restrict__ part_acc,
+                         float* __restrict__ part_ml,
+                         int R, int Hq, int Hkv, int G, int RPT, int NT, int CG,
+                         int n_items, int cap, int nrun, int run_slots, int ring, int window,
+                         float c) {
+    constexpr int D = 512;
+    constexpr int QST = D / 32;                 // reduction steps of a score
+    constexpr int DTW = D / 16;                 // 16-wide d tiles of a column
+    constexpr int NIW = WKB / 4;                // DMA instructions (1 KiB rows) per wave of a role
+    constexpr int BLK = row_pos<D, WPAD>(WKB);
+    constexpr int K16 = row_pos<D, WPAD>(16);
+    constexpr int KPF = 4;                      // score steps of K reads in flight
+    constexpr int VG = 4;                       // d tiles per P.V group
+    constexpr int NG = DTW / VG;
+    constexpr int DMA_K_EVERY = QST / NIW;
+    static_assert(DMA_K_EVERY * NIW == QST && NG == NIW, "DMA spread");
+
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2][BLK];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[2][BLK];
+    __shared__ __attribute__((aligned(16))) u32x4 p_lds[2][4][3][64];   // P^T pieces
+    __shared__ float a_lds[2][4][16];                                   // rescale factors
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool scorer = wave < 4;
+    const int rw = wave & 3;                    // the wave's column tile within the workgroup
+    const int lane = tid & 63;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+
+    // workgroup -> item as in the four-wave kernel
+    const int L = blockIdx.x;
+    const int cgi = (L >> 3) % CG;
+    const int u = ((L >> 3) / CG) * 8 + (L & 7);
+    if (u >= n_items) return;
+    const int run = u % nrun;
+    const int g = (u / nrun) % Hkv;
+    const int s = u / (nrun * Hkv);
+
+    const int ct = cgi * 4 + rw;
+    const int rr = ct * RPT + col / G;
+    const int h = g * G + col % G;
+    const bool cv = ct < NT && col < RPT * G && rr < R;
+    const int p0 = pos[s];
+    const int t_col = cv ? p0 + rr : -1;
+    const int r_lo = cgi * 4 * RPT;
+    const int r_hi = min(R, (cgi + 1) * 4 * RPT) - 1;
+    const int t1 = p0 + r_hi;
+    const int t0 = max(p0 + r_lo, 0);
+    const int w_all = window > 0 ? window + (t1 - t0) : 0;
+    const size_t pidx = (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * (size_t)nrun + run;
+    const int t1m = t1 >= 0 ? t1 % cap : 0;
+    const int tcm = t_col >= 0 ? t_col % cap : 0;
+    auto attended = [&](int slot, int t, int tm, int w) -> bool {
+        int d = tm - slot;
+        d += d < 0 ? cap : 0;
+        const int p = ring ? t - d : slot;
+        return (slot < cap) & (t >= 0) & (p >= 0) & (p <= t) & ((w <= 0) | (t - p < w));
+    };
+
+    const int slot0 = run * run_slots;
+    const int nslot = min(run_slots, cap - slot0);
+    const int nblk = (nslot + WKB - 1) / WKB;
+    int bb_lo = 0x7FFFFFFF, bb_hi = -1;
+    for (int b0 = 0; b0 < nblk; b0 += 8) {
+        const int bb = b0 + (lane >> 3);
+        bool mine = false;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            mine |= (bb < nblk) & attended(slot0 + bb * WKB + 4 * (lane & 7) + i, t1, t1m, w_all);
+        const uint64_t bal = __ballot(mine);
+        if (bal != 0) {
+            bb_lo = min(bb_lo, b0 + __builtin_ctzll(bal) / 8);
+            bb_hi = b0 + (63 - __builtin_clzll(bal)) / 8;
+        }
+    }
+
+    // a run with no attended key leaves an empty partial (m = -inf, l = 0)
+    if (bb_hi < 0) {
+        if (!cv) return;
+        if (scorer) {
+            if (grp == 0) {
+                part_ml[2 * pidx + 0] = -INFINITY;
+                part_ml[2 * pidx + 1] = 0.f;
+            }
+        } else {
+            float* dst = part_acc + pidx * D + 4 * grp;
+#pragma unroll
+            for (int dt = 0; dt < DTW; ++dt)
+                *reinterpret_cast<f32x4*>(dst + 16 * dt) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        return;
+    }
+
+    const size_t head_base = ((size_t)s * Hkv + g) * (size_t)cap * D;
+    const uint16_t* Kh = kc + head_base;
+    const uint16_t* Vh = vc + head_base;
+    const int sub = ring ? t1 % cap : min(t1, cap - 1);     // t1 >= 0 here
+    // DMA rows of this wave: rw + 4 k (K by the scorers, V by the P.V waves)
+    int dma_row[NIW];
+    uint32_t dma_voff[NIW];
+#pragma unroll
+    for (int k = 0; k < NIW; ++k) {
+        dma_row[k] = rw + 4 * k;
+        dma_voff[k] = (uint32_t)(dma_row[k] * D + lane * 8) * 2u;
+    }
+    auto block_all = [&](int b) -> bool {
+        const int sb = slot0 + b * WKB;
+        const bool wrap = ring & (t1m >= sb) & (t1m < sb + WKB - 1);
+        return (sb + WKB <= cap) & !wrap & attended(sb, t1, t1m, w_all) &
+               attended(sb + WKB - 1, t1, t1m, w_all);
+    };
+    auto dma_plan = [&](int b, uint32_t (&vo)[NIW]) {
+        if (block_all(b)) {
+            const uint32_t boff = (uint32_t)(slot0 + b * WKB) * (uint32_t)D * 2u;
+#pragma unroll
+            for (int k = 0; k < NIW; ++k) vo[k] = boff + dma_voff[k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < NIW; ++k) {
+                int slot = slot0 + b * WKB + dma_row[k];
+                slot = attended(slot, t1, t1m, w_all) ? slot : sub;
+                vo[k] = (uint32_t)(slot * D + lane * 8) * 2u;
+            }
+        }
+    };
+    auto dma_one = [&](const uint16_t* base, uint16_t* stage, const uint32_t (&vo)[NIW], int k) {
+        if constexpr (NTL) dma16_asm_sbase_nt(base, vo[k], lds_addr(stage + row_pos<D, WPAD>(dma_row[k])));
+        else dma16_asm_sbase(base, vo[k], lds_addr(stage + row_pos<D, WPAD>(dma_row[k])));
+    };
+    const int t0r = p0 + r_lo;
+    auto block_nomask = [&](int b) -> bool {
+        const int sb = slot0 + b * WKB;
+        int d = t1m - sb;
+        d += d < 0 ? cap : 0;
+        const int pl = ring ? t1 - d : sb;
+        return block_all(b) && t0r >= 0 && pl + WKB - 1 <= t0r &&
+               (window <= 0 || pl >= t1 - window + 1);
+    };
+    auto step_sync = [&]() {
+        __builtin_amdgcn_s_waitcnt(0);           // this wave's DMAs and LDS traffic
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    };
+
+    if (scorer) {
+        float m_run = -INFINITY, l_run = 0.f;
+        // Q^T operand: Q[column][32 st + 8 grp .. +7]
+        u32x4 qreg[QST];
+        const uint16_t* qrow = q + (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * D + 8 * grp;
+#pragma unroll
+        for (int st = 0; st < QST; ++st) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            qreg[st] = cv ? ld16(qrow + 32 * st) : z;
+        }
+        const int kofs = row_pos<D, WPAD>(col) + 8 * grp;
+        {
+            uint32_t vo[NIW];
+            dma_plan(bb_lo, vo);
+#pragma unroll
+            for (int k = 0; k < NIW; ++k) dma_one(Kh, ks[0], vo, k);
+        }
+        // step k scores block bb_lo + k; the last step is the P.V waves'
+        for (int b = bb_lo; b <= bb_hi; ++b) {
+            step_sync();
+            const int sb = (b - bb_lo) & 1;
+            const bool more = b + 1 <= bb_hi;
+            uint32_t kvo[NIW];
+            if (more) dma_plan(b + 1, kvo);
+            const bool nomask = block_nomask(b);
+            const uint16_t* kl = ks[sb];
+            u32x4 kb[KPF][2];
+#pragma unroll
+            for (int j = 0; j < KPF; ++j) {
+                kb[j][0] = ld16(kl + kofs + 32 * j);
+                kb[j][1] = ld16(kl + K16 + kofs + 32 * j);
+            }
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < QST; ++j) {
+                s0 = mfma_bf16_16x16x32(kb[j % KPF][0], qreg[j], s0);
+                s1 = mfma_bf16_16x16x32(kb[j % KPF][1], qreg[j], s1);
+                if (j + KPF < QST) {
+                    kb[j % KPF][0] = ld16(kl + kofs + 32 * (j + KPF));
+                    kb[j % KPF][1] = ld16(kl + K16 + kofs + 32 * (j + KPF));
+                }
+                if (more && j % DMA_K_EVERY == 0) dma_one(Kh, ks[sb ^ 1], kvo, j / DMA_K_EVERY);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const int sbase = slot0 + b * WKB;
+            float tv[8];
+            float mx = -INFINITY;
+            if (nomask) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    tv[e] = s0[e] * c;
+                    tv[4 + e] = s1[e] * c;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok0 = attended(sbase + 4 * grp + e, t_col, tcm, window);
+                    const bool ok1 = attended(sbase + 16 + 4 * grp + e, t_col, tcm, window);
+                    tv[e] = ok0 ? s0[e] * c : -INFINITY;
+                    tv[4 + e] = ok1 ? s1[e] * c : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(tv[e], tv[4 + e]));
+            // reference maximum: moves only when the block maximum passes it
+            // by more than 8 (p <= 2^8); the factor goes to the P.V wave
+            mx = xmax4(mx);
+            const bool grow = mx > m_run + 8.f;
+            float alpha = 1.f;
+            if (__any(grow)) {
+                const float m_new = grow ? mx : m_run;
+                alpha = grow ? fast_exp2(m_run - mx) : 1.f;
+                l_run *= alpha;
+                m_run = m_new;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            float psum = 0.f;
+            uint32_t ph[4], pm[4], pl[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float pa = fast_exp2(tv[2 * k] - m_use);
+                const float pb = fast_exp2(tv[2 * k + 1] - m_use);
+                psum += pa + pb;
+                ph[k] = cvt_pk_bf16(pa, pb);
+                const float ra = pa - bf16lo_to_f32(ph[k]);
+                const float rb = pb - bf16hi_to_f32(ph[k]);
+                pm[k] = cvt_pk_bf16(ra, rb);
+                pl[k] = cvt_pk_bf16(ra - bf16lo_to_f32(pm[k]), rb - bf16hi_to_f32(pm[k]));
+            }
+            l_run += psum;
+            p_lds[sb][rw][0][lane] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+            p_lds[sb][rw][1][lane] = u32x4{pm[0], pm[1], pm[2], pm[3]};
+            p_lds[sb][rw][2][lane] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+            if (grp == 0) a_lds[sb][rw][col] = alpha;
+        }
+        step_sync();
+        const float l_tot = xsum4(l_run);
+        if (cv && grp == 0) {
+            part_ml[2 * pidx + 0] = m_run;
+            part_ml[2 * pidx + 1] = l_tot;
+        }
+        return;
+    }
+    {
+        // V^T operand as in the four-wave kernel (one wave holds all 512 dims)
+        const int vofs = row_pos<D, WPAD>(4 * grp + (col >> 2)) + 4 * (col & 3);
+        f32x4 acc[DTW];
+#pragma unroll
+        for (int dt = 0; dt < DTW; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // V(bb_lo) goes out while the scorers take block bb_lo; step k + 1
+        // multiplies block bb_lo + k
+        {
+            uint32_t vo[NIW];
+            dma_plan(bb_lo, vo);
+#pragma unroll
+            for (int k = 0; k < NIW; ++k) dma_one(Vh, vs[0], vo, k);
+        }
+        step_sync();
+        for (int i = bb_lo; i <= bb_hi; ++i) {
+            const bool more = i + 1 <= bb_hi;
+            uint32_t vvo[NIW];
+            if (more) dma_plan(i + 1, vvo);
+            const int sn = (i + 1 - bb_lo) & 1;  // stage of V(i + 1)
+            step_sync();
+            const int sb = (i - bb_lo) & 1;
+            const uint16_t* vl = vs[sb];
+            auto rd_v = [&](int dt) -> u32x4 {
+                const u32x2 x0 = lds_read_tr16(vl + vofs + 16 * dt);
+                const u32x2 x1 = lds_read_tr16(vl + K16 + vofs + 16 * dt);
+                return u32x4{x0.x, x0.y, x1.x, x1.y};
+            };
+            u32x4 va[2][VG];
+#pragma unroll
+            for (int e = 0; e < VG; ++e) va[0][e] = rd_v(e);
+            const u32x4 bp[3] = {p_lds[sb][rw][0][lane], p_lds[sb][rw][1][lane],
+                                 p_lds[sb][rw][2][lane]};
+            const float alpha = a_lds[sb][rw][col];
+            if (__any(alpha != 1.f)) {
+#pragma unroll
+                for (int dt = 0; dt < DTW; ++dt) acc[dt] *= alpha;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                if (gi + 1 < NG) {
+#pragma unroll
+                    for (int e = 0; e < VG; ++e) va[(gi + 1) & 1][e] = rd_v((gi + 1) * VG + e);
+                }
+#pragma unroll
+                for (int x = 0; x < 3; ++x)
+#pragma unroll
+                    for (int e = 0; e < VG; ++e)
+                        acc[gi * VG + e] = mfma_bf16_16x16x32(va[gi & 1][e], bp[x], acc[gi * VG + e]);
+                if (more) dma_one(Vh, vs[sn], vvo, gi);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (!cv) return;
+        float* dst = part_acc + pidx * D + 4 * grp;
+#pragma unroll
+        for (int dt = 0; dt < DTW; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = acc[dt];
+    }
+}
+
 // Merge of chunk partials in ascending chunk order.  A block of MW waves
 // serves one (stream, head) and 64 VEC d (VEC per lane); wave w takes the
 // contiguous chunk range [w nch / MW, (w + 1) nch / MW) in ascending order,
@@ -948,9 +1282,10 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
     const int G = Hq / Hkv;
     const int RPT = 16 / G;                      // rows per 16-column tile
     const int NT = (R + RPT - 1) / RPT;          // column tiles of a window
-    // four waves a workgroup: at head dim 512 one tile split four ways over
-    // d, two tiles two ways, or four tiles (three leave one wave idle); at
-    // head dim 256 one tile, two block sets by two d halves
+    // at head dim 512 one tile split four ways over d, two tiles two ways
+    // (four waves), or four tiles (eight waves in two roles; three tiles
+    // leave a pair of waves idle); at head dim 256 one tile, two block sets
+    // by two d halves
     const int DS = D == 256 ? 2 : (NT == 1 ? 4 : (NT == 2 ? 2 : 1));
     const int WC = D == 256 ? 1 : 4 / DS;
     const int CG = (NT + WC - 1) / WC;           // workgroups per item
@@ -998,8 +1333,21 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
             else ROWS_LAUNCH(256, 2, false, false);
         }
     } else {
-        if (one) ROWS_DS(512, true);
-        else ROWS_DS(512, false);
+        if (one) {
+            ROWS_DS(512, true);
+        } else if (DS == 1 && !prep) {
+            // four tiles a workgroup: the two-role form on eight waves
+            if (ntl)
+                decode_roles_kernel<true><<<(unsigned)nwg, 512, 0, stream>>>(
+                    q, kc, vc, pos, part_acc, part_ml, R, Hq, Hkv, G, RPT, NT, CG, (int)n_items,
+                    cap, nrun, run_slots, ring, window, c);
+            else
+                decode_roles_kernel<false><<<(unsigned)nwg, 512, 0, stream>>>(
+                    q, kc, vc, pos, part_acc, part_ml, R, Hq, Hkv, G, RPT, NT, CG, (int)n_items,
+                    cap, nrun, run_slots, ring, window, c);
+        } else {
+            ROWS_DS(512, false);
+        }
     }
 #undef ROWS_DS
 #undef ROWS_LAUNCH
