@@ -107,8 +107,8 @@ constexpr int MW = 16;
 // NTL: K/V blocks loaded nontemporal (streamed past the caches), for
 // launches whose K/V span outgrows the last-level cache, so that nothing of
 // it would be there for a later read anyway.
-template <int D, int DS, bool FUSE, bool PREP, bool NTL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, int DS, bool FUSE, bool PREP, bool NTL, bool ONEP = false>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ONEP ? 2 : 1, ONEP ? 2 : 1)))
 void decode_rows_kernel(const uint16_t* __restrict__ q,
                         const uint16_t* __restrict__ kc,
                         const uint16_t* __restrict__ vc,
@@ -146,7 +146,10 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     // those move K and V one block ahead, with no barrier inside a block
     constexpr bool K2 = DS >= 2 && !FUSE && !KP;
     // stages: two blocks (KP: two pairs of blocks, one in use, one landing)
-    constexpr int NST = KP ? 4 : 2;
+    // ONEP (head dim 256, runs of one block pair): two stages, so that two
+    // workgroups share a CU
+    static_assert(!ONEP || (KP && !PREP), "one-pair runs");
+    constexpr int NST = KP && !ONEP ? 4 : 2;
     static_assert(NIW * 4 == NI && NG * VG == DTW && QST >= KPF && (2 * NIW) % QST == 0,
                   "shapes");
 
@@ -319,7 +322,7 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     // rows attend) into stages 2 ((j - jlo) & 1) + {0, 1}
     const int jlo = bb_lo >> 1, jhi = bb_hi >> 1;
     auto issue_pair = [&](int j) {
-        const int sp = 2 * ((j - jlo) & 1);
+        const int sp = ONEP ? 0 : 2 * ((j - jlo) & 1);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
             const int b = 2 * j + e;
@@ -541,7 +544,7 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
             // been read)
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            const int sp = 2 * ((j - jlo) & 1);
+            const int sp = ONEP ? 0 : 2 * ((j - jlo) & 1);
             if constexpr (PREP) {
                 if (j == (b_slot >> 1) && b_slot >= 0) {
                     // the row's own key and value over the staged slot
@@ -558,7 +561,7 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
                     __syncthreads();
                 }
             }
-            if (j + 1 <= jhi) issue_pair(j + 1);
+            if (!ONEP && j + 1 <= jhi) issue_pair(j + 1);
             const int b = 2 * j + set;
             if (b >= bb_lo && b <= bb_hi) block(b, sp + set, std::false_type{}, std::false_type{});
         }
@@ -1324,12 +1327,25 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
         else ROWS_LAUNCH(DD, 1, FF, false);                                                   \
     } while (0)
     if (prep && R != 1) return hipErrorInvalidValue;       // the prologue serves one row
+    // head dim 256, runs of one block pair: the two-stage form
+#define ROWS_ONEP(FF)                                                                         \
+    do {                                                                                      \
+        if (ntl) decode_rows_kernel<256, 2, FF, false, true, true><<<(unsigned)nwg, 256, 0, stream>>>( \
+            q, kc, vc, pos, part_acc, part_ml, out, counters, R, Hq, Hkv, G, RPT, NT, CG,     \
+            (int)n_items, cap, nrun, run_slots, ring, window, c, pa);                         \
+        else decode_rows_kernel<256, 2, FF, false, false, true><<<(unsigned)nwg, 256, 0, stream>>>( \
+            q, kc, vc, pos, part_acc, part_ml, out, counters, R, Hq, Hkv, G, RPT, NT, CG,     \
+            (int)n_items, cap, nrun, run_slots, ring, window, c, pa);                         \
+    } while (0)
+    const bool onep = run_slots <= 2 * WKB && !prep;
     if (D == 256) {
         if (one) {
             if (prep) ROWS_LAUNCH(256, 2, true, true);
+            else if (onep) ROWS_ONEP(true);
             else ROWS_LAUNCH(256, 2, true, false);
         } else {
             if (prep) ROWS_LAUNCH(256, 2, false, true);
+            else if (onep) ROWS_ONEP(false);
             else ROWS_LAUNCH(256, 2, false, false);
         }
     } else {
@@ -1349,6 +1365,7 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
             ROWS_DS(512, false);
         }
     }
+#undef ROWS_ONEP
 #undef ROWS_DS
 #undef ROWS_LAUNCH
 #undef ROWS_LAUNCH_NT
