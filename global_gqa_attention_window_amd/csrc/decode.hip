@@ -96,6 +96,86 @@ constexpr long long DECODE_STREAM_BYTES = 256ll << 20;
 // workgroup that merges in place mirrors its summation order.
 constexpr int MW = 16;
 
+// The slots of one run (slot0 .. slot0 + run_slots - 1) that a workgroup's
+// rows, at positions t0r .. t1, attend.  A slot one of them attends is one
+// the last row attends under the window widened by t1 - max(t0r, 0).  t mod
+// cap is taken once (t1m): a ring slot's position for a row at t is then
+// t - ((t mod cap) - slot, plus cap when negative), with no division.  The
+// tests are written with selects only, so callers' instruction order is
+// never cut by branches.
+struct RunKeys {
+    int cap, ring, window, slot0, t0r, t1, t1m, w_all;
+    ATTN_DEV RunKeys(int cap_, int ring_, int window_, int slot0_, int t_first, int t_last)
+        : cap(cap_), ring(ring_), window(window_), slot0(slot0_), t0r(t_first), t1(t_last),
+          t1m(t_last >= 0 ? t_last % cap_ : 0),
+          w_all(window_ > 0 ? window_ + (t_last - max(t_first, 0)) : 0) {}
+    // slot attended by a row at t (tm = t mod cap) under window w
+    ATTN_DEV bool attended(int slot, int t, int tm, int w) const {
+        int d = tm - slot;
+        d += d < 0 ? cap : 0;
+        const int p = ring ? t - d : slot;
+        return (slot < cap) & (t >= 0) & (p >= 0) & (p <= t) & ((w <= 0) | (t - p < w));
+    }
+    // slot attended by some row of the workgroup
+    ATTN_DEV bool any_row(int slot) const { return attended(slot, t1, t1m, w_all); }
+    // first and last of the run's nblk blocks that hold a slot some row
+    // attends (a wave-wide ballot; hi = -1 when there is none)
+    ATTN_DEV void blocks(int nblk, int lane, int& lo, int& hi) const {
+        lo = 0x7FFFFFFF;
+        hi = -1;
+        for (int b0 = 0; b0 < nblk; b0 += 8) {
+            const int bb = b0 + (lane >> 3);     // lane covers 4 slots of block bb
+            bool mine = false;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                mine |= (bb < nblk) & any_row(slot0 + bb * WKB + 4 * (lane & 7) + i);
+            const uint64_t bal = __ballot(mine);
+            if (bal != 0) {
+                lo = min(lo, b0 + __builtin_ctzll(bal) / 8);
+                hi = b0 + (63 - __builtin_clzll(bal)) / 8;
+            }
+        }
+    }
+    // block b: all its slots attended by the workgroup's rows, holding
+    // consecutive positions (no ring wrap inside; almost every block)
+    ATTN_DEV bool block_all(int b) const {
+        const int sb = slot0 + b * WKB;
+        const bool wrap = ring & (t1m >= sb) & (t1m < sb + WKB - 1);
+        return (sb + WKB <= cap) & !wrap & any_row(sb) & any_row(sb + WKB - 1);
+    }
+    // block b needs no mask: every row attends it whole (its consecutive
+    // positions within [last row - W + 1, first row])
+    ATTN_DEV bool block_nomask(int b) const {
+        const int sb = slot0 + b * WKB;
+        int d = t1m - sb;
+        d += d < 0 ? cap : 0;
+        const int pl = ring ? t1 - d : sb;
+        return block_all(b) && t0r >= 0 && pl + WKB - 1 <= t0r &&
+               (window <= 0 || pl >= t1 - window + 1);
+    }
+    // Sources of block b's DMA rows row[k] as byte offsets (below 2^32) from
+    // the head's K or V base; lane_elem is the lane's element offset in its
+    // row.  A block_all block adds its offset to the fixed per-lane offsets
+    // voff; any other block computes each lane's slot, fetching an unattended
+    // one from slot sub instead.
+    template <int D, int N>
+    ATTN_DEV void dma_plan(int b, int sub, const int (&row)[N], const uint32_t (&voff)[N],
+                           int lane_elem, uint32_t (&vo)[N]) const {
+        if (block_all(b)) {
+            const uint32_t boff = (uint32_t)(slot0 + b * WKB) * (uint32_t)D * 2u;
+#pragma unroll
+            for (int k = 0; k < N; ++k) vo[k] = boff + voff[k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < N; ++k) {
+                int slot = slot0 + b * WKB + row[k];
+                slot = any_row(slot) ? slot : sub;
+                vo[k] = (uint32_t)(slot * D + lane_elem) * 2u;
+            }
+        }
+    }
+};
+
 // FUSE: one launch.  With one run the workgroup writes the output itself
 // (its weight e^(m - m) is 1); otherwise the last workgroup of a (stream, KV
 // head, column group) to finish, found by a counter that it resets, merges
@@ -183,44 +263,19 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     const bool cv = ct < NT && col < RPT * G && rr < R;
     const int p0 = pos[s];
     const int t_col = cv ? p0 + rr : -1;
-    // the workgroup's rows t0..t1: a slot one of them attends is one the last
-    // row attends under a window widened by t1 - t0
+    // the workgroup's rows and the run's slots they attend
     const int r_lo = cgi * WC * RPT;
     const int r_hi = min(R, (cgi + 1) * WC * RPT) - 1;
-    const int t1 = p0 + r_hi;
-    const int t0 = max(p0 + r_lo, 0);
-    const int w_all = window > 0 ? window + (t1 - t0) : 0;
-    const size_t pidx = (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * (size_t)nrun + run;
-    // t mod cap, taken once: a ring slot's position for a row at t is then
-    // t - ((t mod cap) - slot, plus cap when negative), with no division
-    const int t1m = t1 >= 0 ? t1 % cap : 0;
-    const int tcm = t_col >= 0 ? t_col % cap : 0;
-    // slot attended by a row at t (tm = t mod cap) under window w; written
-    // with selects only, so the callers' instruction order is never cut by
-    // branches
-    auto attended = [&](int slot, int t, int tm, int w) -> bool {
-        int d = tm - slot;
-        d += d < 0 ? cap : 0;
-        const int p = ring ? t - d : slot;
-        return (slot < cap) & (t >= 0) & (p >= 0) & (p <= t) & ((w <= 0) | (t - p < w));
-    };
-
     const int slot0 = run * run_slots;
+    const RunKeys rk(cap, ring, window, slot0, p0 + r_lo, p0 + r_hi);
+    const int t1 = rk.t1;
+    const size_t pidx = (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * (size_t)nrun + run;
+    const int tcm = t_col >= 0 ? t_col % cap : 0;
+
     const int nslot = min(run_slots, cap - slot0);
     const int nblk = (nslot + WKB - 1) / WKB;
-    int bb_lo = 0x7FFFFFFF, bb_hi = -1;
-    for (int b0 = 0; b0 < nblk; b0 += 8) {
-        const int bb = b0 + (lane >> 3);         // lane covers 4 slots of block bb
-        bool mine = false;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            mine |= (bb < nblk) & attended(slot0 + bb * WKB + 4 * (lane & 7) + i, t1, t1m, w_all);
-        const uint64_t bal = __ballot(mine);
-        if (bal != 0) {
-            bb_lo = min(bb_lo, b0 + __builtin_ctzll(bal) / 8);
-            bb_hi = b0 + (63 - __builtin_clzll(bal)) / 8;
-        }
-    }
+    int bb_lo, bb_hi;
+    rk.blocks(nblk, lane, bb_lo, bb_hi);
     f32x4 acc[DTW];
 #pragma unroll
     for (int dt = 0; dt < DTW; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -245,7 +300,7 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         // lowest or highest attended slot of block bb (which holds one; an
         // empty ballot would keep the last row's slot)
         auto ends = [&](int bb, bool lowest) {
-            const bool a = lane < WKB && attended(slot0 + bb * WKB + lane, t1, t1m, w_all);
+            const bool a = lane < WKB && rk.any_row(slot0 + bb * WKB + lane);
             const uint64_t bal = __ballot(a);
             if (bal == 0) return sub;
             return slot0 + bb * WKB + (lowest ? __builtin_ctzll(bal) : 63 - __builtin_clzll(bal));
@@ -269,53 +324,18 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         dma_row[k] = (LPR == 64) ? r0 : r0 + 8 * (lane >> 5);
         dma_dst[k] = row_pos<D, WPAD>(r0);
     }
-    // Sources of a block's DMA, as byte offsets (below 2^32) from the head's
-    // K or V base: a block whose 32 slots are all attended by the workgroup's
-    // rows and hold consecutive positions (no ring wrap inside; almost every
-    // block) adds a wave-uniform block offset to per-lane offsets fixed for
-    // the kernel; any other block computes each lane's slot, fetching an
-    // unattended one from the last row's slot instead.
+    // per-lane DMA source offsets of a block with consecutive slots (RunKeys::dma_plan)
     uint32_t dma_voff[NIW];
 #pragma unroll
     for (int k = 0; k < NIW; ++k)
         dma_voff[k] = (uint32_t)(dma_row[k] * D + (lane % LPR) * 8) * 2u;
-    // (bitwise, without short-circuit branches)
-    auto block_all = [&](int b) -> bool {
-        const int sb = slot0 + b * WKB;
-        const bool wrap = ring & (t1m >= sb) & (t1m < sb + WKB - 1);
-        return (sb + WKB <= cap) & !wrap & attended(sb, t1, t1m, w_all) &
-               attended(sb + WKB - 1, t1, t1m, w_all);
-    };
     // block b's DMA offsets from the heads' bases Kh, Vh
     auto dma_plan = [&](int b, uint32_t (&vo)[NIW]) {
-        if (block_all(b)) {
-            const uint32_t boff = (uint32_t)(slot0 + b * WKB) * (uint32_t)D * 2u;
-#pragma unroll
-            for (int k = 0; k < NIW; ++k) vo[k] = boff + dma_voff[k];
-        } else {
-#pragma unroll
-            for (int k = 0; k < NIW; ++k) {
-                int slot = slot0 + b * WKB + dma_row[k];
-                slot = attended(slot, t1, t1m, w_all) ? slot : sub;
-                vo[k] = (uint32_t)(slot * D + (lane % LPR) * 8) * 2u;
-            }
-        }
+        rk.dma_plan<D>(b, sub, dma_row, dma_voff, (lane % LPR) * 8, vo);
     };
     auto dma_one = [&](const uint16_t* base, uint16_t* stage, const uint32_t (&vo)[NIW], int k) {
         if constexpr (NTL) dma16_asm_sbase_nt(base, vo[k], lds_addr(stage + dma_dst[k]));
         else dma16_asm_sbase(base, vo[k], lds_addr(stage + dma_dst[k]));
-    };
-    // a block every row of the workgroup attends whole needs no mask: all
-    // its slots attended together, its positions (consecutive) within
-    // [last row - W + 1, first row]
-    const int t0r = p0 + r_lo;
-    auto block_nomask = [&](int b) -> bool {
-        const int sb = slot0 + b * WKB;
-        int d = t1m - sb;
-        d += d < 0 ? cap : 0;
-        const int pl = ring ? t1 - d : sb;
-        return block_all(b) && t0r >= 0 && pl + WKB - 1 <= t0r &&
-               (window <= 0 || pl >= t1 - window + 1);
     };
 
     // KP: block pair j (blocks 2 j, 2 j + 1 of the run, those the workgroup's
@@ -417,7 +437,7 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         uint32_t nvo[NIW], kvo[NIW];             // DMA plans of V(b + 1), K(b + 2)
         if constexpr (NEXT) dma_plan(b + 1, nvo);
         if constexpr (NEXT2) dma_plan(b + 2, kvo);
-        const bool nomask = block_nomask(b);
+        const bool nomask = rk.block_nomask(b);
         u32x4 kb[KPF][2];
 #pragma unroll
         for (int j = 0; j < KPF; ++j) {
@@ -478,8 +498,8 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const bool ok0 = attended(sb + 4 * grp + i, t_col, tcm, window);
-                const bool ok1 = attended(sb + 16 + 4 * grp + i, t_col, tcm, window);
+                const bool ok0 = rk.attended(sb + 4 * grp + i, t_col, tcm, window);
+                const bool ok1 = rk.attended(sb + 16 + 4 * grp + i, t_col, tcm, window);
                 tv[i] = ok0 ? s0[i] * c : -INFINITY;
                 tv[4 + i] = ok1 ? s1[i] * c : -INFINITY;
             }
@@ -838,35 +858,16 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
     const int t_col = cv ? p0 + rr : -1;
     const int r_lo = cgi * 4 * RPT;
     const int r_hi = min(R, (cgi + 1) * 4 * RPT) - 1;
-    const int t1 = p0 + r_hi;
-    const int t0 = max(p0 + r_lo, 0);
-    const int w_all = window > 0 ? window + (t1 - t0) : 0;
-    const size_t pidx = (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * (size_t)nrun + run;
-    const int t1m = t1 >= 0 ? t1 % cap : 0;
-    const int tcm = t_col >= 0 ? t_col % cap : 0;
-    auto attended = [&](int slot, int t, int tm, int w) -> bool {
-        int d = tm - slot;
-        d += d < 0 ? cap : 0;
-        const int p = ring ? t - d : slot;
-        return (slot < cap) & (t >= 0) & (p >= 0) & (p <= t) & ((w <= 0) | (t - p < w));
-    };
-
     const int slot0 = run * run_slots;
+    const RunKeys rk(cap, ring, window, slot0, p0 + r_lo, p0 + r_hi);
+    const int t1 = rk.t1;
+    const size_t pidx = (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * (size_t)nrun + run;
+    const int tcm = t_col >= 0 ? t_col % cap : 0;
+
     const int nslot = min(run_slots, cap - slot0);
     const int nblk = (nslot + WKB - 1) / WKB;
-    int bb_lo = 0x7FFFFFFF, bb_hi = -1;
-    for (int b0 = 0; b0 < nblk; b0 += 8) {
-        const int bb = b0 + (lane >> 3);
-        bool mine = false;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            mine |= (bb < nblk) & attended(slot0 + bb * WKB + 4 * (lane & 7) + i, t1, t1m, w_all);
-        const uint64_t bal = __ballot(mine);
-        if (bal != 0) {
-            bb_lo = min(bb_lo, b0 + __builtin_ctzll(bal) / 8);
-            bb_hi = b0 + (63 - __builtin_clzll(bal)) / 8;
-        }
-    }
+    int bb_lo, bb_hi;
+    rk.blocks(nblk, lane, bb_lo, bb_hi);
 
     // a run with no attended key leaves an empty partial (m = -inf, l = 0)
     if (bb_hi < 0) {
@@ -897,38 +898,12 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
         dma_row[k] = rw + 4 * k;
         dma_voff[k] = (uint32_t)(dma_row[k] * D + lane * 8) * 2u;
     }
-    auto block_all = [&](int b) -> bool {
-        const int sb = slot0 + b * WKB;
-        const bool wrap = ring & (t1m >= sb) & (t1m < sb + WKB - 1);
-        return (sb + WKB <= cap) & !wrap & attended(sb, t1, t1m, w_all) &
-               attended(sb + WKB - 1, t1, t1m, w_all);
-    };
     auto dma_plan = [&](int b, uint32_t (&vo)[NIW]) {
-        if (block_all(b)) {
-            const uint32_t boff = (uint32_t)(slot0 + b * WKB) * (uint32_t)D * 2u;
-#pragma unroll
-            for (int k = 0; k < NIW; ++k) vo[k] = boff + dma_voff[k];
-        } else {
-#pragma unroll
-            for (int k = 0; k < NIW; ++k) {
-                int slot = slot0 + b * WKB + dma_row[k];
-                slot = attended(slot, t1, t1m, w_all) ? slot : sub;
-                vo[k] = (uint32_t)(slot * D + lane * 8) * 2u;
-            }
-        }
+        rk.dma_plan<D>(b, sub, dma_row, dma_voff, lane * 8, vo);
     };
     auto dma_one = [&](const uint16_t* base, uint16_t* stage, const uint32_t (&vo)[NIW], int k) {
         if constexpr (NTL) dma16_asm_sbase_nt(base, vo[k], lds_addr(stage + row_pos<D, WPAD>(dma_row[k])));
         else dma16_asm_sbase(base, vo[k], lds_addr(stage + row_pos<D, WPAD>(dma_row[k])));
-    };
-    const int t0r = p0 + r_lo;
-    auto block_nomask = [&](int b) -> bool {
-        const int sb = slot0 + b * WKB;
-        int d = t1m - sb;
-        d += d < 0 ? cap : 0;
-        const int pl = ring ? t1 - d : sb;
-        return block_all(b) && t0r >= 0 && pl + WKB - 1 <= t0r &&
-               (window <= 0 || pl >= t1 - window + 1);
     };
     auto step_sync = [&]() {
         __builtin_amdgcn_s_waitcnt(0);           // this wave's DMAs and LDS traffic
@@ -961,7 +936,7 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
             const bool more = b + 1 <= bb_hi;
             uint32_t kvo[NIW];
             if (more) dma_plan(b + 1, kvo);
-            const bool nomask = block_nomask(b);
+            const bool nomask = rk.block_nomask(b);
             const uint16_t* kl = ks[sb];
             u32x4 kb[KPF][2];
 #pragma unroll
@@ -994,8 +969,8 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const bool ok0 = attended(sbase + 4 * grp + e, t_col, tcm, window);
-                    const bool ok1 = attended(sbase + 16 + 4 * grp + e, t_col, tcm, window);
+                    const bool ok0 = rk.attended(sbase + 4 * grp + e, t_col, tcm, window);
+                    const bool ok1 = rk.attended(sbase + 16 + 4 * grp + e, t_col, tcm, window);
                     tv[e] = ok0 ? s0[e] * c : -INFINITY;
                     tv[4 + e] = ok1 ? s1[e] * c : -INFINITY;
                 }
