@@ -20,12 +20,13 @@
 // two roles' products, reads and softmax interleave.  A step is one barrier:
 // the scorers take block i + 1 while the P.V waves take block i (P handed
 // over through two LDS stages).  K and V blocks arrive by direct global->LDS
-// loads issued from asm (two stages each, rows padded by 32 bytes), spread
-// one instruction every few products, K by the scorers and V by the P.V
-// waves; each workgroup rotates its row order so an XCD's concurrent
-// requests spread over the L2 channels.  Every step's arithmetic is the one
-// the two-waves-per-head-pair layout gave (the same partial sums in the same
-// order), so the outputs do not depend on the split.
+// loads issued from asm (two stages each, rows padded by 32 bytes), K by
+// the scorers (one instruction every few score products) and V by the P.V
+// waves (one beside each of the first d tiles' products); each workgroup
+// rotates its row order so an XCD's concurrent requests spread over the L2
+// channels.  Every step's arithmetic is the one the two-waves-per-head-pair
+// layout gave (the same partial sums in the same order), so the outputs do
+// not depend on the split.
 #include "common.h"
 #include "kernels.h"
 
@@ -53,9 +54,10 @@ void prefill_roles_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict
     constexpr int NS = KT * QS;              // K operands per block
     constexpr int KPF = 4;                   // K operand reads in flight
     constexpr int VPF = 4;                   // V^T operands read ahead
-    constexpr int DMA_K_EVERY = NS / IPW;
-    constexpr int DMA_V_EVERY = DTH / IPW;
-    static_assert(DMA_K_EVERY * IPW == NS && DMA_V_EVERY * IPW == DTH, "DMA spread");
+    constexpr int DMA_K_EVERY = NS / IPW;    // K rows: one every few score products
+    // V rows: one beside each of the first IPW d tiles' products, so that
+    // they land well before the step's end
+    static_assert(DMA_K_EVERY * IPW == NS && IPW <= DTH, "DMA spread");
 
     __shared__ __attribute__((aligned(16))) uint16_t ks_lds[2][BLK];
     __shared__ __attribute__((aligned(16))) uint16_t vs_lds[2][BLK];
@@ -349,7 +351,7 @@ void prefill_roles_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict
                     oacc[k][dt] = mfma_bf16_16x16x32(a, ph[k], oacc[k][dt]);
                     if (X2) oacc[k][dt] = mfma_bf16_16x16x32(a, pl[k], oacc[k][dt]);
                 }
-                if (more && dt % DMA_V_EVERY == 0) dma_issue(vbase, vvoff, vlds, dt / DMA_V_EVERY);
+                if (more && dt < IPW) dma_issue(vbase, vvoff, vlds, dt);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else if (more) {
