@@ -825,8 +825,12 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
     constexpr int KPF = 4;                      // score steps of K reads in flight
     constexpr int VG = 4;                       // d tiles per P.V group
     constexpr int NG = DTW / VG;
-    constexpr int DMA_K_EVERY = QST / NIW;
-    static_assert(DMA_K_EVERY * NIW == QST && NG == NIW, "DMA spread");
+    constexpr int DMA_K_EVERY = QST / NIW;      // K rows: one every few score products
+    // V rows: half beside each of the first two P.V groups, so that they land
+    // well before the step's end
+    constexpr int DMA_V_GROUPS = 2;
+    static_assert(DMA_K_EVERY * NIW == QST && NIW % DMA_V_GROUPS == 0 && DMA_V_GROUPS <= NG,
+                  "DMA spread");
 
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][BLK];
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][BLK];
@@ -1066,7 +1070,11 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
 #pragma unroll
                     for (int e = 0; e < VG; ++e)
                         acc[gi * VG + e] = mfma_bf16_16x16x32(va[gi & 1][e], bp[x], acc[gi * VG + e]);
-                if (more) dma_one(Vh, vs[sn], vvo, gi);
+                if (more && gi < DMA_V_GROUPS) {
+#pragma unroll
+                    for (int kk = 0; kk < NIW / DMA_V_GROUPS; ++kk)
+                        dma_one(Vh, vs[sn], vvo, gi * (NIW / DMA_V_GROUPS) + kk);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
