@@ -141,7 +141,8 @@ struct RunKeys {
     ATTN_DEV bool block_all(int b) const {
         const int sb = slot0 + b * WKB;
         const bool wrap = ring & (t1m >= sb) & (t1m < sb + WKB - 1);
-        return (sb + WKB <= cap) & !wrap & any_row(sb) & any_row(sb + WKB - 1);
+        return ((int)(sb + WKB <= cap) & (int)!wrap & (int)any_row(sb) &
+                (int)any_row(sb + WKB - 1)) != 0;
     }
     // block b needs no mask: every row attends it whole (its consecutive
     // positions within [last row - W + 1, first row])
@@ -790,22 +791,24 @@ void decode_rows_kernel(const uint16_t* __restrict__ q,
     }
 }
 
-// Decode windows at head dim 512 over four column tiles a workgroup (the
-// shapes that give one tile to each of four waves above), in two roles on
-// eight waves, two per SIMD, as the head-dim-512 prompt kernel splits its
-// work: scorer w (waves 0-3) forms tile w's scores, reference maximum and
-// probability pieces and hands the pieces and the rescale factor over
-// through LDS; P.V wave w (waves 4-7) holds tile w's accumulator over all
-// 512 dims and adds V^T . {hi, mid, lo} to it.  With one wave a SIMD a
-// wave's K reads and softmax cannot hide behind its own products; here the
-// scorer of block b + 1 and the P.V wave of block b share each SIMD.  A step
-// is one barrier: scorers take block i + 1 (K(i + 1) in stage (i + 1) - lo,
+// Decode windows of four column tiles a workgroup (three or more tiles a
+// window; fewer tiles go to the kernel above), in two roles on eight waves,
+// two per SIMD, as the head-dim-512 prompt kernel splits its work: scorer w
+// (waves 0-3) forms tile w's scores, reference maximum and probability
+// pieces and hands the pieces and the rescale factor over through LDS; P.V
+// wave w (waves 4-7) holds tile w's accumulator over all D dims and adds
+// V^T . {hi, mid, lo} to it.  With one wave a SIMD a wave's K reads and
+// softmax cannot hide behind its own products; here the scorer of block
+// b + 1 and the P.V wave of block b share each SIMD.  A step is one
+// barrier: scorers take block i + 1 (K(i + 1) in stage (i + 1) - lo,
 // loading K(i + 2)) while the P.V waves take block i (V(i), loading
-// V(i + 1)).  Every column's arithmetic is the four-wave kernel's, step for
-// step (the same score chains, the same lazy maximum, the same pieces, the
-// same product order per accumulator), so the bits are those of every other
-// form and do not depend on the window width.
-template <bool NTL>
+// V(i + 1)).  Every column's arithmetic is the kernel above's, step for step
+// (the same score chains, the same lazy maximum, the same pieces, the same
+// product order per accumulator; at head dim 256 its two block sets, the
+// run's even and odd blocks, each with its own maximum, sum and
+// accumulator, joined once at the end), so the bits are those of every
+// other form and do not depend on the window width.
+template <int D, bool NTL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_roles_kernel(const uint16_t* __restrict__ q,
                          const uint16_t* __restrict__ kc,
@@ -816,14 +819,17 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
                          int R, int Hq, int Hkv, int G, int RPT, int NT, int CG,
                          int n_items, int cap, int nrun, int run_slots, int ring, int window,
                          float c) {
-    constexpr int D = 512;
     constexpr int QST = D / 32;                 // reduction steps of a score
     constexpr int DTW = D / 16;                 // 16-wide d tiles of a column
-    constexpr int NIW = WKB / 4;                // DMA instructions (1 KiB rows) per wave of a role
+    constexpr int LPR = D / 8;                  // lanes moving one row per DMA
+    constexpr int NIW = WKB * LPR / 64 / 4;     // DMA instructions per wave of a role per block
+    constexpr int NSET = D == 256 ? 2 : 1;      // block sets (even and odd blocks at 256)
     constexpr int BLK = row_pos<D, WPAD>(WKB);
     constexpr int K16 = row_pos<D, WPAD>(16);
     constexpr int KPF = 4;                      // score steps of K reads in flight
-    constexpr int VG = 4;                       // d tiles per P.V group
+    // d tiles per P.V group (at 256 the two sets' accumulators leave room for
+    // fewer V^T operands in flight)
+    constexpr int VG = D == 256 ? 2 : 4;
     constexpr int NG = DTW / VG;
     constexpr int DMA_K_EVERY = QST / NIW;      // K rows: one every few score products
     // V rows: half beside each of the first two P.V groups, so that they land
@@ -836,6 +842,7 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][BLK];
     __shared__ __attribute__((aligned(16))) u32x4 p_lds[2][4][3][64];   // P^T pieces
     __shared__ float a_lds[2][4][16];                                   // rescale factors
+    __shared__ float j_lds[4][2][16];           // the block sets' weights (two sets)
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -845,7 +852,7 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
     const int col = lane & 15;
     const int grp = lane >> 4;
 
-    // workgroup -> item as in the four-wave kernel
+    // workgroup -> item as in the kernel above
     const int L = blockIdx.x;
     const int cgi = (L >> 3) % CG;
     const int u = ((L >> 3) / CG) * 8 + (L & 7);
@@ -894,20 +901,26 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
     const uint16_t* Kh = kc + head_base;
     const uint16_t* Vh = vc + head_base;
     const int sub = ring ? t1 % cap : min(t1, cap - 1);     // t1 >= 0 here
-    // DMA rows of this wave: rw + 4 k (K by the scorers, V by the P.V waves)
+    // DMA instruction i = rw + 4 k of a K or V block moves 1 KiB: block row
+    // i at D = 512, rows 16 (i >> 3) + (i & 7) and + 8 at D = 256 (lanes
+    // 0..31, 32..63); K by the scorers, V by the P.V waves
     int dma_row[NIW];
+    int dma_dst[NIW];
     uint32_t dma_voff[NIW];
 #pragma unroll
     for (int k = 0; k < NIW; ++k) {
-        dma_row[k] = rw + 4 * k;
-        dma_voff[k] = (uint32_t)(dma_row[k] * D + lane * 8) * 2u;
+        const int i = rw + 4 * k;
+        const int r0 = (LPR == 64) ? i : 16 * (i >> 3) + (i & 7);
+        dma_row[k] = (LPR == 64) ? r0 : r0 + 8 * (lane >> 5);
+        dma_dst[k] = row_pos<D, WPAD>(r0);
+        dma_voff[k] = (uint32_t)(dma_row[k] * D + (lane % LPR) * 8) * 2u;
     }
     auto dma_plan = [&](int b, uint32_t (&vo)[NIW]) {
-        rk.dma_plan<D>(b, sub, dma_row, dma_voff, lane * 8, vo);
+        rk.dma_plan<D>(b, sub, dma_row, dma_voff, (lane % LPR) * 8, vo);
     };
     auto dma_one = [&](const uint16_t* base, uint16_t* stage, const uint32_t (&vo)[NIW], int k) {
-        if constexpr (NTL) dma16_asm_sbase_nt(base, vo[k], lds_addr(stage + row_pos<D, WPAD>(dma_row[k])));
-        else dma16_asm_sbase(base, vo[k], lds_addr(stage + row_pos<D, WPAD>(dma_row[k])));
+        if constexpr (NTL) dma16_asm_sbase_nt(base, vo[k], lds_addr(stage + dma_dst[k]));
+        else dma16_asm_sbase(base, vo[k], lds_addr(stage + dma_dst[k]));
     };
     auto step_sync = [&]() {
         __builtin_amdgcn_s_waitcnt(0);           // this wave's DMAs and LDS traffic
@@ -917,7 +930,13 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
     };
 
     if (scorer) {
-        float m_run = -INFINITY, l_run = 0.f;
+        // per block set: reference maximum and per-lane row sum
+        float m_run[NSET], l_run[NSET];
+#pragma unroll
+        for (int e = 0; e < NSET; ++e) {
+            m_run[e] = -INFINITY;
+            l_run[e] = 0.f;
+        }
         // Q^T operand: Q[column][32 st + 8 grp .. +7]
         u32x4 qreg[QST];
         const uint16_t* qrow = q + (((size_t)s * R + (cv ? rr : 0)) * Hq + h) * D + 8 * grp;
@@ -933,9 +952,8 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
 #pragma unroll
             for (int k = 0; k < NIW; ++k) dma_one(Kh, ks[0], vo, k);
         }
-        // step k scores block bb_lo + k; the last step is the P.V waves'
-        for (int b = bb_lo; b <= bb_hi; ++b) {
-            step_sync();
+        // block b with its set's maximum and sum
+        auto score_block = [&](int b, float& m_cur, float& l_cur) {
             const int sb = (b - bb_lo) & 1;
             const bool more = b + 1 <= bb_hi;
             uint32_t kvo[NIW];
@@ -984,15 +1002,15 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
             // reference maximum: moves only when the block maximum passes it
             // by more than 8 (p <= 2^8); the factor goes to the P.V wave
             mx = xmax4(mx);
-            const bool grow = mx > m_run + 8.f;
+            const bool grow = mx > m_cur + 8.f;
             float alpha = 1.f;
             if (__any(grow)) {
-                const float m_new = grow ? mx : m_run;
-                alpha = grow ? fast_exp2(m_run - mx) : 1.f;
-                l_run *= alpha;
-                m_run = m_new;
+                const float m_new = grow ? mx : m_cur;
+                alpha = grow ? fast_exp2(m_cur - mx) : 1.f;
+                l_cur *= alpha;
+                m_cur = m_new;
             }
-            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            const float m_use = (m_cur == -INFINITY) ? 0.f : m_cur;
             float psum = 0.f;
             uint32_t ph[4], pm[4], pl[4];
 #pragma unroll
@@ -1006,36 +1024,55 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
                 pm[k] = cvt_pk_bf16(ra, rb);
                 pl[k] = cvt_pk_bf16(ra - bf16lo_to_f32(pm[k]), rb - bf16hi_to_f32(pm[k]));
             }
-            l_run += psum;
+            l_cur += psum;
             p_lds[sb][rw][0][lane] = u32x4{ph[0], ph[1], ph[2], ph[3]};
             p_lds[sb][rw][1][lane] = u32x4{pm[0], pm[1], pm[2], pm[3]};
             p_lds[sb][rw][2][lane] = u32x4{pl[0], pl[1], pl[2], pl[3]};
             if (grp == 0) a_lds[sb][rw][col] = alpha;
+        };
+        // step k scores block bb_lo + k; the last step is the P.V waves'
+        for (int b = bb_lo; b <= bb_hi; ++b) {
+            step_sync();
+            if (NSET == 2 && (b & 1)) score_block(b, m_run[NSET - 1], l_run[NSET - 1]);
+            else score_block(b, m_run[0], l_run[0]);
         }
         step_sync();
-        const float l_tot = xsum4(l_run);
+        float m_fin = m_run[0], l_fin = l_run[0];
+        if constexpr (NSET == 2) {
+            // the two sets joined per lane: M = the larger maximum, each set
+            // weighted by 2^(m - M) (0 for a set with no attended key); the
+            // P.V wave applies the same weights to its two accumulators
+#pragma clang fp contract(off)
+            const float M = fmaxf(m_run[0], m_run[1]);
+            const float w0 = m_run[0] == -INFINITY ? 0.f : fast_exp2(m_run[0] - M);
+            const float w1 = m_run[1] == -INFINITY ? 0.f : fast_exp2(m_run[1] - M);
+            const float l0w = l_run[0] * w0;
+            const float l1w = l_run[1] * w1;
+            l_fin = l0w + l1w;
+            m_fin = M;
+            if (grp == 0) {
+                j_lds[rw][0][col] = w0;
+                j_lds[rw][1][col] = w1;
+            }
+            step_sync();
+        }
+        const float l_tot = xsum4(l_fin);
         if (cv && grp == 0) {
-            part_ml[2 * pidx + 0] = m_run;
+            part_ml[2 * pidx + 0] = m_fin;
             part_ml[2 * pidx + 1] = l_tot;
         }
         return;
     }
     {
-        // V^T operand as in the four-wave kernel (one wave holds all 512 dims)
+        // V^T operand as in the kernel above (one wave holds all D dims)
         const int vofs = row_pos<D, WPAD>(4 * grp + (col >> 2)) + 4 * (col & 3);
-        f32x4 acc[DTW];
+        f32x4 acc[NSET][DTW];
 #pragma unroll
-        for (int dt = 0; dt < DTW; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // V(bb_lo) goes out while the scorers take block bb_lo; step k + 1
-        // multiplies block bb_lo + k
-        {
-            uint32_t vo[NIW];
-            dma_plan(bb_lo, vo);
+        for (int e = 0; e < NSET; ++e)
 #pragma unroll
-            for (int k = 0; k < NIW; ++k) dma_one(Vh, vs[0], vo, k);
-        }
-        step_sync();
-        for (int i = bb_lo; i <= bb_hi; ++i) {
+            for (int dt = 0; dt < DTW; ++dt) acc[e][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // block i into its set's accumulator
+        auto pv_block = [&](int i, f32x4 (&ac)[DTW]) {
             const bool more = i + 1 <= bb_hi;
             uint32_t vvo[NIW];
             if (more) dma_plan(i + 1, vvo);
@@ -1056,7 +1093,7 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
             const float alpha = a_lds[sb][rw][col];
             if (__any(alpha != 1.f)) {
 #pragma unroll
-                for (int dt = 0; dt < DTW; ++dt) acc[dt] *= alpha;
+                for (int dt = 0; dt < DTW; ++dt) ac[dt] *= alpha;
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1069,7 +1106,7 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
                 for (int x = 0; x < 3; ++x)
 #pragma unroll
                     for (int e = 0; e < VG; ++e)
-                        acc[gi * VG + e] = mfma_bf16_16x16x32(va[gi & 1][e], bp[x], acc[gi * VG + e]);
+                        ac[gi * VG + e] = mfma_bf16_16x16x32(va[gi & 1][e], bp[x], ac[gi * VG + e]);
                 if (more && gi < DMA_V_GROUPS) {
 #pragma unroll
                     for (int kk = 0; kk < NIW / DMA_V_GROUPS; ++kk)
@@ -1077,11 +1114,40 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+        };
+        // V(bb_lo) goes out while the scorers take block bb_lo; step k + 1
+        // multiplies block bb_lo + k
+        {
+            uint32_t vo[NIW];
+            dma_plan(bb_lo, vo);
+#pragma unroll
+            for (int k = 0; k < NIW; ++k) dma_one(Vh, vs[0], vo, k);
+        }
+        step_sync();
+        for (int i = bb_lo; i <= bb_hi; ++i) {
+            if (NSET == 2 && (i & 1)) pv_block(i, acc[NSET - 1]);
+            else pv_block(i, acc[0]);
+        }
+        if constexpr (NSET == 2) {
+            step_sync();                         // the scorer's set weights
+            {
+#pragma clang fp contract(off)
+                const float w0 = j_lds[rw][0][col];
+                const float w1 = j_lds[rw][1][col];
+#pragma unroll
+                for (int dt = 0; dt < DTW; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float a0 = acc[0][dt][i] * w0;
+                        const float a1 = acc[1][dt][i] * w1;
+                        acc[0][dt][i] = a0 + a1;
+                    }
+            }
         }
         if (!cv) return;
         float* dst = part_acc + pidx * D + 4 * grp;
 #pragma unroll
-        for (int dt = 0; dt < DTW; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = acc[dt];
+        for (int dt = 0; dt < DTW; ++dt) *reinterpret_cast<f32x4*>(dst + 16 * dt) = acc[0][dt];
     }
 }
 
@@ -1216,6 +1282,60 @@ void decode_merge_kernel(uint16_t* __restrict__ out,
     }
 }
 
+// Merge of at most MW runs: the merge kernel's arithmetic with one wave per
+// (stream, head) and d slice.  There each wave holds one run or none, its
+// sum being the run's weighted terms rounded once (fmaf from +0), and the
+// waves' sums add in ascending order.  A sum that starts at +0 is never -0,
+// so adding an empty wave's +0 changes nothing: here each run's terms add in
+// ascending run order directly, every run's loads in flight at once and no
+// exchange through LDS.
+template <int D>
+__global__ __launch_bounds__(64)
+void decode_merge_few_kernel(uint16_t* __restrict__ out,
+                             const float* __restrict__ part_acc,
+                             const float* __restrict__ part_ml,
+                             int nch) {
+#pragma clang fp contract(off)
+    const int sh = blockIdx.x;                 // s * Hq + h
+    const int lane = threadIdx.x;
+    const int d0 = blockIdx.y * 256 + lane * 4;
+    const size_t base = (size_t)sh * (size_t)nch;
+    const float2* ml = reinterpret_cast<const float2*>(part_ml) + base;
+    float2 e[MW];
+    f32x4 a[MW];
+#pragma unroll
+    for (int c = 0; c < MW; ++c) {
+        if (c < nch) {
+            e[c] = ml[c];
+            a[c] = *reinterpret_cast<const f32x4*>(part_acc + (base + c) * D + d0);
+        } else {
+            e[c] = float2{-INFINITY, 0.f};
+            a[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < MW; ++c) M = fmaxf(M, e[c].x);
+    float Lt = 0.f;
+    f32x4 ot = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int c = 0; c < MW; ++c) {
+            if (e[c].x == -INFINITY) continue;
+            const float wt = fast_exp2(e[c].x - M);
+            Lt = Lt + fmaf(wt, e[c].y, 0.f);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ot[i] = ot[i] + fmaf(wt, a[c][i], 0.f);
+        }
+    }
+    uint32_t bb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        bb[i] = (Lt != 0.f || Lt != Lt) ? f32_to_bf16_bits(ot[i] / Lt) : 0u;
+    uint16_t* orow = out + (size_t)sh * D + d0;
+    *reinterpret_cast<u32x2*>(orow) = u32x2{pack_bf16x2(bb[0], bb[1]), pack_bf16x2(bb[2], bb[3])};
+}
+
 }  // namespace
 
 size_t decode_workspace_bytes(int S, int Hq, int D, int cap) {
@@ -1246,6 +1366,15 @@ static hipError_t launch_decode_merge(uint16_t* out, const float* part_acc, cons
     const long long wide = (long long)n_rows_heads * (D / 256);
     const int vec = (nrun < 64 || wide >= 512) ? 4 : (2 * wide >= 512 ? 2 : 1);
     const dim3 g2(n_rows_heads, D / (64 * vec));
+    if (nrun <= MW) {
+        // at most MW runs: one wave per (stream, head) and 256-wide d slice
+        // (vec is 4 here)
+        if (D == 256)
+            decode_merge_few_kernel<256><<<g2, 64, 0, stream>>>(out, part_acc, part_ml, nrun);
+        else
+            decode_merge_few_kernel<512><<<g2, 64, 0, stream>>>(out, part_acc, part_ml, nrun);
+        return hipGetLastError();
+    }
 #define MERGE_LAUNCH(DD, VV) \
     decode_merge_kernel<DD, VV><<<g2, 64 * MW, 0, stream>>>(out, part_acc, part_ml, nrun)
     if (D == 256) {
@@ -1268,21 +1397,26 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
     const int G = Hq / Hkv;
     const int RPT = 16 / G;                      // rows per 16-column tile
     const int NT = (R + RPT - 1) / RPT;          // column tiles of a window
-    // at head dim 512 one tile split four ways over d, two tiles two ways
-    // (four waves), or four tiles (eight waves in two roles; three tiles
-    // leave a pair of waves idle); at head dim 256 one tile, two block sets
-    // by two d halves
-    const int DS = D == 256 ? 2 : (NT == 1 ? 4 : (NT == 2 ? 2 : 1));
-    const int WC = D == 256 ? 1 : 4 / DS;
-    const int CG = (NT + WC - 1) / WC;           // workgroups per item
     const int run_slots = decode_run_slots(cap);
     const int nrun = decode_run_count(cap);
-    const long long n_items = (long long)nrun * Hkv * S;
-    const long long nwg = (n_items + 7) / 8 * 8 * CG;
-    if (nwg > 0x7FFFFFFFLL || (long long)S * R * Hq > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     // one launch when the merge fits a workgroup (at most MW runs); the
     // counters sit at the start of a fused call's workspace
     const bool one = fused && nrun <= MW;
+    // windows of three or more tiles: four tiles a workgroup, eight waves in
+    // two roles (three tiles leave a scorer and a P.V wave idle); at head dim
+    // 256 only while that still gives 128 workgroups or more (a tile a
+    // workgroup spreads a small window wider).  Otherwise four waves: at head
+    // dim 512 one tile split four ways over d, two tiles two ways (or four
+    // tiles in the single launch); at head dim 256 one tile, two block sets
+    // by two d halves.  Every form gives the same bits.
+    const long long n_items = (long long)nrun * Hkv * S;
+    const bool roles = !one && !prep && NT >= 3 &&
+                       (D == 512 || n_items * ((NT + 3) / 4) >= 128);
+    const int DS = D == 256 ? 2 : (NT == 1 ? 4 : (NT == 2 ? 2 : 1));
+    const int WC = roles ? 4 : (D == 256 ? 1 : 4 / DS);
+    const int CG = (NT + WC - 1) / WC;           // workgroups per item
+    const long long nwg = (n_items + 7) / 8 * 8 * CG;
+    if (nwg > 0x7FFFFFFFLL || (long long)S * R * Hq > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     uint32_t* counters = reinterpret_cast<uint32_t*>(ws);
     float* part_acc = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                                (fused ? ATTN_DECODE_COUNTER_BYTES : 0));
@@ -1320,8 +1454,20 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
             q, kc, vc, pos, part_acc, part_ml, out, counters, R, Hq, Hkv, G, RPT, NT, CG,     \
             (int)n_items, cap, nrun, run_slots, ring, window, c, pa);                         \
     } while (0)
+#define ROLES_LAUNCH(DD)                                                                      \
+    do {                                                                                      \
+        if (ntl) decode_roles_kernel<DD, true><<<(unsigned)nwg, 512, 0, stream>>>(            \
+            q, kc, vc, pos, part_acc, part_ml, R, Hq, Hkv, G, RPT, NT, CG, (int)n_items, cap, \
+            nrun, run_slots, ring, window, c);                                                \
+        else decode_roles_kernel<DD, false><<<(unsigned)nwg, 512, 0, stream>>>(               \
+            q, kc, vc, pos, part_acc, part_ml, R, Hq, Hkv, G, RPT, NT, CG, (int)n_items, cap, \
+            nrun, run_slots, ring, window, c);                                                \
+    } while (0)
     const bool onep = run_slots <= 2 * WKB && !prep;
-    if (D == 256) {
+    if (roles) {
+        if (D == 256) ROLES_LAUNCH(256);
+        else ROLES_LAUNCH(512);
+    } else if (D == 256) {
         if (one) {
             if (prep) ROWS_LAUNCH(256, 2, true, true);
             else if (onep) ROWS_ONEP(true);
@@ -1332,22 +1478,10 @@ hipError_t launch_decode_rows(uint16_t* out, const uint16_t* q, const uint16_t* 
             else ROWS_LAUNCH(256, 2, false, false);
         }
     } else {
-        if (one) {
-            ROWS_DS(512, true);
-        } else if (DS == 1 && !prep) {
-            // four tiles a workgroup: the two-role form on eight waves
-            if (ntl)
-                decode_roles_kernel<true><<<(unsigned)nwg, 512, 0, stream>>>(
-                    q, kc, vc, pos, part_acc, part_ml, R, Hq, Hkv, G, RPT, NT, CG, (int)n_items,
-                    cap, nrun, run_slots, ring, window, c);
-            else
-                decode_roles_kernel<false><<<(unsigned)nwg, 512, 0, stream>>>(
-                    q, kc, vc, pos, part_acc, part_ml, R, Hq, Hkv, G, RPT, NT, CG, (int)n_items,
-                    cap, nrun, run_slots, ring, window, c);
-        } else {
-            ROWS_DS(512, false);
-        }
+        if (one) ROWS_DS(512, true);
+        else ROWS_DS(512, false);
     }
+#undef ROLES_LAUNCH
 #undef ROWS_ONEP
 #undef ROWS_DS
 #undef ROWS_LAUNCH
