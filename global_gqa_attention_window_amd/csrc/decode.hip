@@ -33,17 +33,17 @@ constexpr int CHUNK = ATTN_DECODE_CHUNK;
 // workgroup's waves.  At head dim 512 a workgroup takes 4 / DS column tiles
 // of one (stream, KV head, run of chunks); the DS waves of a tile split its
 // output d range (all of them form the tile's scores, so a column's
-// arithmetic is the same for every DS); two block stages.  Four tiles go to
-// decode_roles_kernel, which splits each tile's work between a scorer wave
-// and a P.V wave with the same per-column arithmetic.  At head dim 256 a
-// workgroup takes one tile: the run's even blocks go to waves 0 and 1 and its
-// odd blocks to waves 2 and 3, each pair splitting d in two, so a block's K
-// rows are read and its scores formed by two waves instead of four; each
-// block set keeps its own online softmax and the two join once at the end
-// (M = the larger reference maximum, each set weighted by 2^(m - M)); a pair
-// of blocks lands while the previous pair is multiplied (four stages).  Every
-// R takes the same per-column steps, one tile per workgroup.  Per block and
-// column:
+// arithmetic is the same for every DS); two block stages.  At head dim 256
+// a workgroup takes one tile: the run's even blocks go to waves 0 and 1 and
+// its odd blocks to waves 2 and 3, each pair splitting d in two, so a
+// block's K rows are read and its scores formed by two waves instead of
+// four; each block set keeps its own online softmax and the two join once
+// at the end (M = the larger reference maximum, each set weighted by
+// 2^(m - M)); a pair of blocks lands while the previous pair is multiplied
+// (four stages).  Windows of three or more tiles go, four tiles a
+// workgroup, to decode_roles_kernel, which splits each tile's work between
+// a scorer wave and a P.V wave with the same per-column arithmetic (at head
+// dim 256 the same two block sets).  Per block and column:
 //   S^T = K . Q^T               bf16 products, two 16-key tiles;
 //   reference maximum           as in the one-row kernel (moves only when the
 //                               block maximum passes it by 8), so p <= 2^8;
