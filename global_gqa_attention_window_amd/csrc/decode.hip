@@ -848,6 +848,9 @@ void decode_roles_kernel(const uint16_t* __restrict__ q,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool scorer = wave < 4;
     const int rw = wave & 3;                    // the wave's column tile within the workgroup
+    // the scorer's K reads and softmax gate the next step; its SIMD's P.V wave fills
+    // the gaps (measured on 8 x 16 rows at 32k keys: 1-2% faster than equal priority)
+    if (scorer) __builtin_amdgcn_s_setprio(1);
     const int lane = tid & 63;
     const int col = lane & 15;
     const int grp = lane >> 4;
