@@ -71,13 +71,20 @@ def test_decode_rows_shapes(ga, D, Hq, Hkv, cap, ring, window, R, pos):
     _check(f"rows D={D} G={Hq // Hkv} R={R} ring={ring} W={window}", got, ref)
 
 
-@pytest.mark.parametrize("D,Hq,Hkv,cap,ring,window", [
-    (512, 32, 2, 4096, 0, 0), (256, 32, 4, 1536, 1, 1024)])
-def test_decode_rows_bits_independent_of_width(ga, D, Hq, Hkv, cap, ring, window):
-    say("decode rows width invariance", D)
-    rng = np.random.default_rng(17 + D)
-    S, R = 2, 16
-    p = np.array([3000, 1500], dtype=np.int32) if ring else np.array([4080, 900], np.int32)
+@pytest.mark.parametrize("D,Hq,Hkv,cap,ring,window,S", [
+    (512, 32, 2, 4096, 0, 0, 2), (256, 32, 4, 1536, 1, 1024, 2),
+    # sixteen streams: enough (stream, KV head, run) items that the full
+    # head-dim-256 window takes the eight-wave two-role form while its single
+    # rows take the four-wave one
+    (256, 32, 4, 1536, 1, 1024, 16)])
+def test_decode_rows_bits_independent_of_width(ga, D, Hq, Hkv, cap, ring, window, S):
+    say("decode rows width invariance", D, S)
+    rng = np.random.default_rng(17 + D if S == 2 else 17 + D + S)
+    R = 16
+    if S == 2:
+        p = np.array([3000, 1500], dtype=np.int32) if ring else np.array([4080, 900], np.int32)
+    else:
+        p = np.array([5000 + 37 * s for s in range(S)], dtype=np.int32)
     q = randn_bf16_bits(rng, (S, R, Hq, D))
     k = randn_bf16_bits(rng, (S, Hkv, cap, D))
     v = randn_bf16_bits(rng, (S, Hkv, cap, D))
