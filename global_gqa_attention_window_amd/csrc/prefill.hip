@@ -120,7 +120,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
                     int ring, int window, float c,
                     const int32_t* __restrict__ last_key, int S,
                     float* __restrict__ part_acc, float* __restrict__ part_ml, int pos_base,
-                    int clamp_rows) {
+                    int clamp_rows, int rs, long long hs) {
     constexpr int KB = PrefillCfg<D>::KB;
     constexpr int KPADP = 16;                // K padding per row (pair at 256)
     constexpr int VPADP = 16;                // V padding per row (pair at 256)
@@ -203,8 +203,10 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         b_end = b_lo + split_start(nb, S, sp + 1) - 1;
     }
 
-    const uint16_t* Kg = kc + (size_t)g * cap * D;
-    const uint16_t* Vg = vc + (size_t)g * cap * D;
+    // key rows of KV group g: slot s at Kg + s rs (a cache: rs = D, groups
+    // cap D apart; a prompt's own k / v rows: rs = Hkv D, groups D apart)
+    const uint16_t* Kg = kc + (size_t)g * (size_t)hs;
+    const uint16_t* Vg = vc + (size_t)g * (size_t)hs;
 
     // DMA of one K or V block: instruction j (wave w issues [w IPW, (w+1) IPW))
     // moves 1 KiB: block row j at D=512, rows 16 (j >> 3) + (j & 7) and +8 at
@@ -234,14 +236,14 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
     const int lane_col = (lane % LPR) * 8;
     uint32_t lane_off[IPW];
 #pragma unroll
-    for (int i = 0; i < IPW; ++i) lane_off[i] = (uint32_t)(lane_row[i] * D + lane_col) * 2u;
+    for (int i = 0; i < IPW; ++i) lane_off[i] = (uint32_t)(lane_row[i] * rs + lane_col) * 2u;
     auto dma_plan = [&](const uint16_t* g, uint16_t* stage, int b, const uint16_t*& base,
                         uint32_t (&voff)[IPW], uint32_t& lds0) {
         const int p0 = b * KB;
         const int s0 = ring ? p0 % cap : p0 - pos_base;
         lds0 = lds_addr(stage);
         if (p0 >= lo_tile && p0 + KB - 1 <= hi_tile && s0 + KB <= cap) {
-            base = g + (size_t)s0 * D;
+            base = g + (size_t)s0 * rs;
 #pragma unroll
             for (int i = 0; i < IPW; ++i) voff[i] = lane_off[i];
         } else {
@@ -250,7 +252,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
             for (int i = 0; i < IPW; ++i) {
                 const int p = min(max(p0 + lane_row[i], lo_tile), hi_tile);
                 const int slot = ring ? p % cap : p - pos_base;
-                voff[i] = (uint32_t)(slot * D + lane_col) * 2u;
+                voff[i] = (uint32_t)(slot * rs + lane_col) * 2u;
             }
         }
     };
@@ -313,7 +315,7 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         const int p = max(min(b * KB + r, hi_tile), lo_tile);
         const int slot = ring ? p % cap : p - pos_base;
         const uint16_t* g = wave == 0 ? Kg : Vg;
-        dma16_asm_sbase(g, (uint32_t)(slot * D + (lane * 8) % D) * 2u,
+        dma16_asm_sbase(g, (uint32_t)(slot * rs + (lane * 8) % D) * 2u,
                         lds_addr(pf_lds[wave]));
     };
 
@@ -822,11 +824,19 @@ hipError_t launch_prefill_attend(uint16_t* out, const uint16_t* q, const uint16_
                                  const uint16_t* vc, int pos0, int n_rows, int Hq, int Hkv,
                                  int D, int cap, int ring, int window, float scale,
                                  int p_mode, const int32_t* last_key, void* ws, int base,
-                                 int clamp_rows, hipStream_t stream, PrefillParts& parts) {
+                                 int clamp_rows, hipStream_t stream, PrefillParts& parts,
+                                 int rs = 0, long long hs = 0) {
     parts = PrefillParts{};
-    if (D == 512)
+    // key row and KV group strides (elements): a cache's unless given
+    if (rs == 0) {
+        rs = D;
+        hs = (long long)cap * D;
+    }
+    if (D == 512) {
+        if (rs != D) return hipErrorInvalidValue;   // that kernel reads caches only
         return launch_prefill_512(out, q, kc, vc, pos0, n_rows, Hq, Hkv, cap, ring, window,
                                   scale, p_mode, last_key, base, clamp_rows, stream);
+    }
     const int G = Hq / Hkv;
     const float c = scale * ATTN_LOG2E;
     const int S = ws ? prefill_split_count(n_rows, Hq, Hkv, D) : 1;
@@ -842,7 +852,7 @@ hipError_t launch_prefill_attend(uint16_t* out, const uint16_t* q, const uint16_
 #define PF_LAUNCH(PP, SP, NN)                                                                 \
     prefill_kernel<256, PP, SP, NN><<<grid, 64 * NN, 0, stream>>>(                            \
         out, q, kc, vc, pos0, n_rows, Hq, Hkv, G, HG, cap, ring, window, c, last_key, S,      \
-        part_acc, part_ml, base, clamp_rows)
+        part_acc, part_ml, base, clamp_rows, rs, hs)
     if (S > 1) {
         if (p_mode == ATTN_P_BF16X2) PF_LAUNCH(ATTN_P_BF16X2, true, 4);
         else PF_LAUNCH(ATTN_P_BF16, true, 4);
@@ -908,22 +918,33 @@ hipError_t launch_prefill_prompt(uint16_t* out, const uint16_t* q, const uint16_
                                      scale, p_mode, last_key, nullptr, 0, chunk, stream, parts);
     }
     // A ring: chunk c + 1's rows would overwrite keys chunk c still reads, so
-    // every key the prompt attends (the window before pos0 from the ring, the
-    // prompt's own from k and v) goes to a linear copy in the workspace, one
-    // launch attends the whole prompt over it, and the prompt's last rows
-    // then enter the ring (those the chunked path leaves there).
+    // one launch attends the whole prompt over a linear copy, in the
+    // workspace, of every key it attends (the window before pos0 from the
+    // ring, the prompt's own from k and v) -- or over k and v themselves when
+    // it attends no key before pos0 -- and the prompt's last rows then enter
+    // the ring (those the chunked path leaves there).
     const int base = std::max(0, pos0 - window + 1);
-    const int L = pos0 + n_rows - base;
-    uint16_t* sk = static_cast<uint16_t*>(ws);
-    uint16_t* sv = sk + (size_t)Hkv * L * D;
-    const size_t units = (size_t)Hkv * L * (D / 8);
-    stage_kernel<<<(unsigned)((units + 255) / 256), 256, 0, stream>>>(sk, sv, kc, vc, k, v, pos0,
-                                                                      base, L, n_rows, Hkv, D,
-                                                                      cap);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = launch_prefill_attend(out, q, sk, sv, pos0, n_rows, Hq, Hkv, D, L, 0, window, scale,
-                              p_mode, last_key, nullptr, base, chunk, stream, parts);
+    hipError_t e;
+    if (D == 256 && window > 0 && base == pos0 &&
+        (long long)n_rows * Hkv * D * 2 < (1LL << 32)) {
+        // no key before pos0 is attended (a prompt from position 0, or a
+        // window of one): every key is one of the prompt's own rows, read in
+        // place from k and v (rows Hkv D apart, groups D apart), no copy
+        e = launch_prefill_attend(out, q, k, v, pos0, n_rows, Hq, Hkv, D, n_rows, 0, window,
+                                  scale, p_mode, last_key, nullptr, pos0, chunk, stream, parts,
+                                  Hkv * D, D);
+    } else {
+        const int L = pos0 + n_rows - base;
+        uint16_t* sk = static_cast<uint16_t*>(ws);
+        uint16_t* sv = sk + (size_t)Hkv * L * D;
+        const size_t units = (size_t)Hkv * L * (D / 8);
+        stage_kernel<<<(unsigned)((units + 255) / 256), 256, 0, stream>>>(
+            sk, sv, kc, vc, k, v, pos0, base, L, n_rows, Hkv, D, cap);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        e = launch_prefill_attend(out, q, sk, sv, pos0, n_rows, Hq, Hkv, D, L, 0, window, scale,
+                                  p_mode, last_key, nullptr, base, chunk, stream, parts);
+    }
     if (e != hipSuccess) return e;
     const int tail = std::min(n_rows, cap);
     const size_t ko = (size_t)(n_rows - tail) * Hkv * D;
