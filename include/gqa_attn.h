@@ -394,8 +394,10 @@ int attn_cache_write(void* k_cache, void* v_cache, const void* k,
  * into a linear cache every row is written first; with a ring, where chunk c
  * + 1 would overwrite keys chunk c still reads, the keys the prompt attends
  * (the window before pos0 from the ring, the prompt's own from k and v) go
- * to a linear copy in the workspace, and the prompt's last rows enter the
- * ring after the attention.
+ * to a linear copy in the workspace -- or, when the prompt attends no key
+ * before pos0 (pos0 = 0, or a window of one) at head dim 256, are read in
+ * place from k and v, leaving the workspace untouched -- and the prompt's
+ * last rows enter the ring after the attention.
  *
  *   out, q            device bf16 [n_rows][Hq][D]
  *   k, v              device bf16 [n_rows][Hkv][D], the prompt's keys and
