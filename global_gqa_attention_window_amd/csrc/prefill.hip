@@ -650,7 +650,13 @@ void prefill_kernel(uint16_t* __restrict__ out, const uint16_t* __restrict__ q,
         auto v_hook = [](int) {};
         if (head_ok) {
             f32x4 sacc[KT];
+            // with eight waves, each SIMD's second (younger) wave issues its
+            // score products at wave priority 1, so it keeps pace with the
+            // first, which the barrier would otherwise make wait for it
+            // (8k prompt about 1% less time; the arithmetic is unchanged)
+            if (NW == 8 && wave >= 4) __builtin_amdgcn_s_setprio(1);
             score_phase(ks_lds[st ^ 1], vs_lds[st], sacc, vb, sm_alpha, k_hook);
+            if (NW == 8 && wave >= 4) __builtin_amdgcn_s_setprio(0);
             if (!is_interior(b + 1)) mask(b + 1, sacc);
             pv_phase(vs_lds[st], vb, pch, pcl, sacc, pnh, pnl, v_hook);
 #pragma unroll
